@@ -1,0 +1,278 @@
+/*
+ * Plain CPU oracle of the decode MoE layer tail -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or helper with the HIP
+ * path; it is written to be read against the pages and checked by eye.
+ *
+ * What it computes, per decode row, all in IEEE double precision:
+ *   h      = bf16(x + r)                    fused residual add (rounded once)
+ *   rstd   = 1 / sqrt(sum(h^2) / H + eps)
+ *   xn     = bf16(h * rstd * gamma)         post-attention RMSNorm output
+ *   l[e]   = sum_i xn[i] * Wr[e, i]         router logits (not rounded)
+ *   key[e] = l[e]              (softmax scoring)
+ *          = sigmoid(l[e]) + b[e]  (sigmoid scoring with a selection bias)
+ *   S      = the K experts with the largest keys, ties to the lower id,
+ *            listed by (key descending, id ascending)
+ *   w      = softmax(l[S])     (softmax scoring; equals p[S]/sum p[S])
+ *          = sigmoid(l[S]) / sum sigmoid(l[S])   (sigmoid scoring)
+ *   for each pick e in S:  [g | u] = deq(W13[e]) xn,  a = g*sigmoid(g)*u,
+ *                          d_e = deq(W2[e]) a
+ *   s      = Ws2 (silu(Ws13_gate xn) * Ws13_up xn)   bf16 shared expert
+ *   y      = sum_k w_k d_{S_k} + s ;   out = bf16(h + y)
+ *
+ * Sources (page titles; no listing is followed line by line):
+ *   - "[AMD] integrate kimi k3 monokernel" (sglang PR 43481), K2 commit text,
+ *     sections Motivation, Refusals and "Kernel Replacement": the tail's steps
+ *     (fused add + RMSNorm, router GEMV, top-k with norm_topk_prob, MXFP4 routed
+ *     experts gate/up + SiLU*up + down, bf16 shared expert, residual output).
+ *   - "glm53: Long-context indexer ..." (sgl-amd-mono PR 86), PR 85 commit
+ *     rows 9 and 20: top-k rounds that resolve exact ties toward the lower id.
+ *   - OCP Microscaling Formats (MX) v1.0: E2M1 element and E8M0 scale
+ *     encodings, blocks of 32 elements (the pages name MXFP4 but do not
+ *     define it).
+ * Readings where the pages are silent (gamma multiplies plainly, eps inside
+ * the square root, gate rows first in W13, low nibble = even element, no
+ * routed scaling factor, no shared-expert gate) are listed with the design
+ * notes of the repository.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- number formats ------------------------------------------------------ */
+
+/* E2M1 magnitudes, OCP MX v1.0 table for FP4: codes 0..7 (bit 3 is the sign). */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1(int code) {
+  double m = kE2M1[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+/* E8M0: 2^(b-127); 0xFF encodes NaN. */
+double oracle_e8m0(int b) {
+  if ((b & 0xFF) == 0xFF) return NAN;
+  return ldexp(1.0, (b & 0xFF) - 127);
+}
+
+double oracle_dequant(int code, int scale_byte) {
+  return oracle_e2m1(code) * oracle_e8m0(scale_byte);
+}
+
+double oracle_bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a double to bfloat16, nearest with ties to even, from the exact value:
+ * 8 significant bits for normals, quantum 2^-133 for subnormals, overflow to
+ * infinity. */
+uint16_t oracle_bf16_round(double v) {
+  if (isnan(v)) return 0x7FC0;
+  double a = fabs(v), q;
+  if (a == 0.0) {
+    q = 0.0;
+  } else {
+    int e;
+    frexp(a, &e); /* a = m 2^e, 0.5 <= m < 1, so a in [2^(e-1), 2^e) */
+    int qexp = e - 8; /* 8 significant bits */
+    if (qexp < -133) qexp = -133;
+    q = ldexp(nearbyint(ldexp(a, -qexp)), qexp); /* default rounding: to even */
+  }
+  float f = (float)q; /* exact: q has <= 8 significant bits */
+  if (q >= ldexp(1.0, 128)) f = INFINITY;
+  if (v < 0.0 || (v == 0.0 && signbit(v))) f = -f;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+/* ---- the layer's steps --------------------------------------------------- */
+
+static double bfd(const uint16_t* p, size_t i) { return oracle_bf16_to_double(p[i]); }
+
+static double sigmoid(double t) { return 1.0 / (1.0 + exp(-t)); }
+
+/* Fused residual add + RMSNorm of one row.  h_out, xn_out: [H] bf16 bits. */
+void oracle_norm_row(int H, double eps, const uint16_t* x, const uint16_t* r, const uint16_t* gamma,
+                     uint16_t* h_out, uint16_t* xn_out, double* rstd_out) {
+  double ss = 0.0;
+  for (int i = 0; i < H; i++) {
+    double s = bfd(x, i) + (r ? bfd(r, i) : 0.0);
+    h_out[i] = oracle_bf16_round(s);
+    double h = bfd(h_out, i);
+    ss += h * h;
+  }
+  double rstd = 1.0 / sqrt(ss / (double)H + eps);
+  for (int i = 0; i < H; i++) xn_out[i] = oracle_bf16_round(bfd(h_out, i) * rstd * bfd(gamma, i));
+  if (rstd_out) *rstd_out = rstd;
+}
+
+/* Router logits of one row: l[e] = sum_i xn[i] Wr[e,i]. */
+void oracle_router_row(int H, int E, const uint16_t* xn, const uint16_t* router_w, double* logits) {
+  for (int e = 0; e < E; e++) {
+    double acc = 0.0;
+    const uint16_t* w = router_w + (size_t)e * H;
+    for (int i = 0; i < H; i++) acc += bfd(xn, i) * bfd(w, i);
+    logits[e] = acc;
+  }
+}
+
+/* Selection keys from logits. scoring 0: key = l; 1: key = sigmoid(l) + bias. */
+void oracle_keys(int E, int scoring, const double* logits, const float* bias, double* keys) {
+  for (int e = 0; e < E; e++) keys[e] = scoring == 0 ? logits[e] : sigmoid(logits[e]) + (double)bias[e];
+}
+
+/* Expert a beats expert b: larger key, or equal key and lower id. */
+static int beats(const double* keys, int a, int b) {
+  return keys[a] > keys[b] || (keys[a] == keys[b] && a < b);
+}
+
+/* Top-K by repeated selection of the best remaining expert. ids[0..K) in
+ * (key descending, id ascending) order. */
+void oracle_topk(int E, int K, const double* keys, int32_t* ids) {
+  char* taken = (char*)calloc((size_t)E, 1);
+  for (int k = 0; k < K; k++) {
+    int best = -1;
+    for (int e = 0; e < E; e++)
+      if (!taken[e] && (best < 0 || beats(keys, e, best))) best = e;
+    ids[k] = best;
+    taken[best] = 1;
+  }
+  free(taken);
+}
+
+/* Normalised top-K weights. */
+void oracle_topk_weights(int K, int scoring, const double* logits, const int32_t* ids, double* w) {
+  double sum = 0.0;
+  if (scoring == 0) {
+    double mx = -INFINITY;
+    for (int k = 0; k < K; k++) mx = fmax(mx, logits[ids[k]]);
+    for (int k = 0; k < K; k++) sum += (w[k] = exp(logits[ids[k]] - mx));
+  } else {
+    for (int k = 0; k < K; k++) sum += (w[k] = sigmoid(logits[ids[k]]));
+  }
+  for (int k = 0; k < K; k++) w[k] /= sum;
+}
+
+/* Dequantized MXFP4 element (row, col) of a [rows, cols] matrix stored as
+ * codes [rows, cols/2] (low nibble = even column) and scales [rows, cols/32]. */
+static double mx_at(const uint8_t* q, const uint8_t* s, int cols, int row, int col) {
+  uint8_t byte = q[(size_t)row * (cols / 2) + col / 2];
+  int code = (col & 1) ? (byte >> 4) : (byte & 0xF);
+  return oracle_dequant(code, s[(size_t)row * (cols / 32) + col / 32]);
+}
+
+/* One routed expert on one row: d[H] = W2 (silu(g) * u), [g|u] = W13 xn. */
+void oracle_expert_row(int H, int I, const uint16_t* xn, const uint8_t* w13_q, const uint8_t* w13_s,
+                       const uint8_t* w2_q, const uint8_t* w2_s, double* a_out, double* d_out) {
+  double* a = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int i = 0; i < I; i++) {
+    double g = 0.0, u = 0.0;
+    for (int j = 0; j < H; j++) {
+      double v = bfd(xn, j);
+      g += mx_at(w13_q, w13_s, H, i, j) * v;
+      u += mx_at(w13_q, w13_s, H, I + i, j) * v;
+    }
+    a[i] = g * sigmoid(g) * u;
+    if (a_out) a_out[i] = a[i];
+  }
+  for (int h = 0; h < H; h++) {
+    double acc = 0.0;
+    for (int i = 0; i < I; i++) acc += mx_at(w2_q, w2_s, I, h, i) * a[i];
+    d_out[h] = acc;
+  }
+  free(a);
+}
+
+/* The bf16 shared expert on one row: s[H]. */
+void oracle_shared_row(int H, int Is, const uint16_t* xn, const uint16_t* ws13, const uint16_t* ws2,
+                       double* s_out) {
+  double* a = (double*)malloc(sizeof(double) * (size_t)Is);
+  for (int i = 0; i < Is; i++) {
+    double g = 0.0, u = 0.0;
+    for (int j = 0; j < H; j++) {
+      double v = bfd(xn, j);
+      g += bfd(ws13, (size_t)i * H + j) * v;
+      u += bfd(ws13, (size_t)(Is + i) * H + j) * v;
+    }
+    a[i] = g * sigmoid(g) * u;
+  }
+  for (int h = 0; h < H; h++) {
+    double acc = 0.0;
+    for (int i = 0; i < Is; i++) acc += bfd(ws2, (size_t)h * Is + i) * a[i];
+    s_out[h] = acc;
+  }
+  free(a);
+}
+
+/* The whole tail for `rows` rows.  Every output pointer may be NULL except
+ * out.  Shapes: x, r, h_out, xn_out, out: [rows, H] bf16 bits; logits, keys:
+ * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H]. */
+int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps,
+                    const uint16_t* x, const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w,
+                    const float* bias, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                    const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, uint16_t* h_out,
+                    uint16_t* xn_out, double* logits_out, double* keys_out, int32_t* ids_out, double* w_out,
+                    double* y_routed_out, double* y_shared_out, uint16_t* out) {
+  if (rows < 0 || H <= 0 || H % 32 || E <= 0 || K <= 0 || K > E || I <= 0 || I % 32 || Is < 0 || !out) return 1;
+  if (scoring == 1 && !bias) return 1;
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  double* lg = (double*)malloc(sizeof(double) * (size_t)E);
+  double* ky = (double*)malloc(sizeof(double) * (size_t)E);
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+  double* w = (double*)malloc(sizeof(double) * (size_t)K);
+  double* d = (double*)malloc(sizeof(double) * (size_t)H);
+  double* yr = (double*)malloc(sizeof(double) * (size_t)H);
+  double* ys = (double*)malloc(sizeof(double) * (size_t)H);
+  const size_t e13 = (size_t)2 * I * (H / 2), e13s = (size_t)2 * I * (H / 32);
+  const size_t e2 = (size_t)H * (I / 2), e2s = (size_t)H * (I / 32);
+  for (int row = 0; row < rows; row++) {
+    const size_t ro = (size_t)row * H;
+    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
+    oracle_router_row(H, E, xn, router_w, lg);
+    oracle_keys(E, scoring, lg, bias, ky);
+    oracle_topk(E, K, ky, ids);
+    oracle_topk_weights(K, scoring, lg, ids, w);
+    for (int j = 0; j < H; j++) yr[j] = 0.0;
+    for (int k = 0; k < K; k++) {
+      const int e = ids[k];
+      oracle_expert_row(H, I, xn, w13_q + e * e13, w13_s + e * e13s, w2_q + e * e2, w2_s + e * e2s, NULL, d);
+      for (int j = 0; j < H; j++) yr[j] += w[k] * d[j];
+    }
+    for (int j = 0; j < H; j++) ys[j] = 0.0;
+    if (Is > 0) oracle_shared_row(H, Is, xn, ws13, ws2, ys);
+    for (int j = 0; j < H; j++) out[ro + j] = oracle_bf16_round(bfd(h, j) + (yr[j] + ys[j]));
+    if (h_out) memcpy(h_out + ro, h, sizeof(uint16_t) * (size_t)H);
+    if (xn_out) memcpy(xn_out + ro, xn, sizeof(uint16_t) * (size_t)H);
+    if (logits_out) memcpy(logits_out + (size_t)row * E, lg, sizeof(double) * (size_t)E);
+    if (keys_out) memcpy(keys_out + (size_t)row * E, ky, sizeof(double) * (size_t)E);
+    if (ids_out) memcpy(ids_out + (size_t)row * K, ids, sizeof(int32_t) * (size_t)K);
+    if (w_out) memcpy(w_out + (size_t)row * K, w, sizeof(double) * (size_t)K);
+    if (y_routed_out) memcpy(y_routed_out + ro, yr, sizeof(double) * (size_t)H);
+    if (y_shared_out) memcpy(y_shared_out + ro, ys, sizeof(double) * (size_t)H);
+  }
+  free(h); free(xn); free(lg); free(ky); free(ids); free(w); free(d); free(yr); free(ys);
+  return 0;
+}
+
+/* Norm + router + keys only (used to check the top-k gap of generated rows). */
+int oracle_router_keys(int rows, int H, int E, int scoring, double eps, const uint16_t* x, const uint16_t* r,
+                       const uint16_t* gamma, const uint16_t* router_w, const float* bias, double* logits_out,
+                       double* keys_out) {
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  for (int row = 0; row < rows; row++) {
+    const size_t ro = (size_t)row * H;
+    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
+    oracle_router_row(H, E, xn, router_w, logits_out + (size_t)row * E);
+    oracle_keys(E, scoring, logits_out + (size_t)row * E, bias, keys_out + (size_t)row * E);
+  }
+  free(h); free(xn);
+  return 0;
+}
