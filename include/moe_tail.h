@@ -1,0 +1,132 @@
+/*
+ * moe_tail.h -- C ABI of the fused decode MoE layer tail for MI355X (gfx950).
+ *
+ * One call runs, for 1..16 decode rows of one tensor-parallel rank's shard,
+ * in a single persistent HIP launch:
+ *
+ *   h       = bf16(x + residual)                      fused residual add
+ *   xn      = bf16(h * rstd * gamma),  rstd = 1/sqrt(mean(h^2) + eps)
+ *   logits  = xn . router_w^T                          (fp32, not rounded)
+ *   top-k   softmax scoring: the K largest logits; weights = softmax over them
+ *           sigmoid scoring: the K largest sigmoid(logit) + bias; weights =
+ *           sigmoid(logit) / sum over the K picks (the bias selects only)
+ *           ties always go to the lower expert id
+ *   routed  for each pick e: a = silu(W13_gate[e] xn) * (W13_up[e] xn),
+ *           d_e = W2[e] a, with MXFP4 weights (E2M1 codes, E8M0 block-32 scales)
+ *   shared  s = Ws2 (silu(Ws13_gate xn) * (Ws13_up xn)), bf16 weights
+ *   out     = bf16(h + sum_k w_k d_{e_k} + s),  res_out = h
+ *
+ * Sources: "[AMD] integrate kimi k3 monokernel" (sglang PR 43481), K2 commit
+ * text, sections Motivation, Refusals and "Kernel Replacement" (the steps of
+ * the tail and its refusals); "glm53: Long-context indexer ..." (sgl-amd-mono
+ * PR 86), PR 85 commit table rows 9, 16, 18, 20, 21 (tie rule, expert
+ * de-duplication, 16-byte and nontemporal weight loads); "Split the Kimi3
+ * AttnRes mix across CTAs for decode rows" (flare PR 11), design section
+ * (chunk-ordered fp32 partial sums, per-call tags); OCP Microscaling v1.0
+ * (MXFP4 encoding).  There is no all-reduce: the result is one rank's
+ * partial sum added to h.
+ *
+ * Conventions.  Every tensor pointer is a device pointer to caller-owned,
+ * row-major, contiguous memory, 16-byte aligned.  The library reads the
+ * weights in place and never copies them.  bf16 tensors are passed as raw
+ * 16-bit patterns (void*).  No function throws; all report a status.
+ */
+#ifndef MOE_TAIL_H
+#define MOE_TAIL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_tail moe_tail_t; /* opaque handle */
+
+typedef enum {
+  MOE_TAIL_OK = 0,
+  MOE_TAIL_EINVAL = 1,        /* bad argument: size, pointer, alignment, rows */
+  MOE_TAIL_EUNSUPPORTED = 2,  /* device is not gfx950, or limits exceeded */
+  MOE_TAIL_ENOMEM = 3,        /* scratch allocation failed */
+  MOE_TAIL_EHIP = 4,          /* a HIP runtime call failed */
+  MOE_TAIL_ETIMEOUT = 5       /* a cross-workgroup wait passed its deadline */
+} moe_tail_status;
+
+typedef enum { MOE_TAIL_SOFTMAX = 0, MOE_TAIL_SIGMOID_BIAS = 1 } moe_tail_scoring;
+
+/* debug_flags bit: the workgroup `debug_block` never proceeds past its first
+ * cross-workgroup wait until that wait's deadline fires (fault drill). */
+#define MOE_TAIL_DEBUG_STALL 1u
+
+typedef struct {
+  int32_t max_rows;     /* largest `rows` any run will pass: 1..16 */
+  int32_t hidden;       /* H: multiple of 128, 128..16384 */
+  int32_t num_experts;  /* E: 1..512 */
+  int32_t top_k;        /* K: 1..min(E, 32) */
+  int32_t inter;        /* I, per-rank expert intermediate: multiple of 32, 32..4096 */
+  int32_t shared_inter; /* Is, per-rank shared intermediate: 0 (none) or multiple of 32, <= 4096 */
+  int32_t scoring;      /* moe_tail_scoring */
+  float eps;            /* RMSNorm epsilon, > 0 */
+  int32_t device;       /* HIP device ordinal, or -1 for the current device */
+  uint32_t deadline_us; /* per-wait deadline in microseconds; 0 selects 200000 */
+  uint32_t debug_flags; /* 0 in production; see MOE_TAIL_DEBUG_STALL */
+  int32_t debug_block;  /* workgroup index used by debug_flags */
+} moe_tail_config;
+
+typedef struct {
+  /* inputs */
+  const void* x;            /* [rows, H] bf16 post-attention activations */
+  const void* residual;     /* [rows, H] bf16, or NULL (then h = x) */
+  const void* gamma;        /* [H] bf16 RMSNorm weight */
+  const void* router_w;     /* [E, H] bf16 */
+  const float* router_bias; /* [E] fp32, required for MOE_TAIL_SIGMOID_BIAS, else ignored */
+  const uint8_t* w13_q;     /* [E, 2I, H/2]: rows [0,I) gate, [I,2I) up; byte j = elements 2j (low nibble), 2j+1 (high) */
+  const uint8_t* w13_s;     /* [E, 2I, H/32] E8M0 scale of each 32-element block along H */
+  const uint8_t* w2_q;      /* [E, H, I/2] down projection codes, same nibble order */
+  const uint8_t* w2_s;      /* [E, H, I/32] E8M0 scales along I */
+  const void* ws13;         /* [2Is, H] bf16 shared gate (rows [0,Is)) and up; NULL iff Is == 0 */
+  const void* ws2;          /* [H, Is] bf16 shared down; NULL iff Is == 0 */
+  /* outputs */
+  void* out;                /* [rows, H] bf16: h + routed + shared */
+  void* res_out;            /* [rows, H] bf16: h, or NULL */
+  int32_t* topk_ids;        /* [rows, K] selected experts, (key desc, id asc) order, or NULL */
+  float* topk_w;            /* [rows, K] normalised weights, or NULL */
+  float* dbg_logits;        /* [rows, E] router logits, or NULL */
+  float* dbg_y_routed;      /* [rows, H] fp32 routed sum, or NULL */
+  float* dbg_y_shared;      /* [rows, H] fp32 shared expert output, or NULL */
+} moe_tail_args;
+
+/* Validate a configuration on the host only (no GPU call).  Returns
+ * MOE_TAIL_OK or MOE_TAIL_EINVAL / MOE_TAIL_EUNSUPPORTED. */
+moe_tail_status moe_tail_check_config(const moe_tail_config* cfg);
+
+/* Create a handle: validates cfg, checks the device is gfx950, allocates the
+ * handle-owned scratch (exchange buffers, counters, error word) sized for
+ * max_rows, and zeroes it.  On failure *out is NULL. */
+moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
+
+/* Enqueue one call on `stream` (a hipStream_t; NULL = default stream) and
+ * return without synchronising.  1 <= rows <= max_rows.  Graph-capturable:
+ * the handle's per-call epoch lives in device memory, so replays need no
+ * host work.  Calls on one handle must be ordered (one stream at a time).
+ * Argument errors are returned synchronously and nothing is enqueued; a
+ * device-side deadline is reported later by moe_tail_get_error. */
+moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_tail_args* args, void* stream);
+
+/* Read and clear the sticky device error word (MOE_TAIL_OK or
+ * MOE_TAIL_ETIMEOUT).  Synchronous; call after the caller has synchronised
+ * the stream of the runs it covers. */
+moe_tail_status moe_tail_get_error(moe_tail_t* h);
+
+/* Text of the last error reported on this handle (or on creation when h is
+ * NULL); valid until the next call on the handle. */
+const char* moe_tail_strerror(moe_tail_t* h);
+
+/* Free the handle and its scratch.  The caller makes sure no run on it is
+ * still in flight. */
+void moe_tail_destroy(moe_tail_t* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_TAIL_H */

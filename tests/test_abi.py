@@ -1,0 +1,70 @@
+"""The C ABI library: builds, loads, exports every declared symbol, and validates on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_moe_layer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe_tail.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_tail_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_struct_layout_matches_header():
+    # moe_tail_config: 11 x 4-byte fields + float; moe_tail_args: 18 pointers
+    assert ctypes.sizeof(binding.Config) == 12 * 4
+    assert ctypes.sizeof(binding.Args) == 18 * 8
+
+
+def good():
+    return binding.make_config(8, 6144, 512, 10, 256, 512)
+
+
+def test_check_config_accepts_the_workloads():
+    assert binding.check_config(good()) == binding.OK
+    for args in [(1, 512, 16, 2, 64, 64), (4, 7168, 256, 8, 256, 256, binding.SIGMOID_BIAS), (16, 8192, 384, 8, 256, 256),
+                 (16, 6144, 512, 10, 256, 512), (3, 1024, 64, 32, 32, 0)]:
+        assert binding.check_config(binding.make_config(*args)) == binding.OK, args
+
+
+@pytest.mark.parametrize("field,value", [
+    ("max_rows", 0), ("max_rows", 17), ("hidden", 100), ("hidden", 6000), ("hidden", 32768),
+    ("num_experts", 0), ("num_experts", 513), ("top_k", 0), ("top_k", 33), ("inter", 48), ("inter", 0),
+    ("shared_inter", 40), ("shared_inter", -32), ("scoring", 2), ("eps", 0.0), ("eps", float("nan")),
+    ("debug_flags", 6),
+])
+def test_check_config_refusals(field, value):
+    c = good()
+    setattr(c, field, value)
+    assert binding.check_config(c) == binding.EINVAL
+    assert binding.strerror(None)
+
+
+def test_topk_above_experts_refused():
+    c = binding.make_config(1, 512, 4, 5, 64, 0)
+    assert binding.check_config(c) == binding.EINVAL
+
+
+def test_create_without_gpu_reports_error():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(binding.MoeTailError) as ei:
+        binding.MoeTail(good())
+    assert ei.value.status in (binding.EHIP, binding.EUNSUPPORTED)
