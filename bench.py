@@ -1,0 +1,280 @@
+"""Benchmark of the fused decode MoE layer tail on one MI355X.
+
+A step is one call of the tail (norm, router, top-k, de-duplicated MXFP4
+routed experts, bf16 shared expert, combine) over one batch of decode rows.
+The headline workload is the one-rank shard at 8 rows (hidden 6144, 512
+experts, top-10, I 256, shared Is 512, rows drawn so ~30 % of picks repeat).
+
+Timing: L copies of the weights at distinct device addresses (so that the
+256 MB Infinity Cache cannot serve a call from a previous call's lines), one
+HIP graph of calls rotating over the copies, replayed; HIP events on the
+launch stream bracket exactly K calls.  Achieved bandwidth is the algorithmic
+bytes of a call (distinct selected experts' codes and scales, router, shared
+expert, gamma, activations in and out) over the measured time per call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep/--no-sweep]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_moe_layer_amd import binding, synth  # noqa: E402
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
+METRIC = "µs per MoE-tail call and achieved HBM GB/s (fraction of peak) at 1/8 rows"
+MALL_BYTES = 256 * 2**20
+
+
+def c2_rho():
+    with open(os.path.join(ROOT, "tests", "golden", "c2_rho.json")) as f:
+        return float(json.load(f)["rho"])
+
+
+def per_expert_bytes(cfg):
+    H, I = cfg.hidden, cfg.inter
+    return 2 * I * H // 2 + 2 * I * H // 32 + H * I // 2 + H * I // 32
+
+
+def alg_bytes(cfg, rows, distinct):
+    H, E, Is = cfg.hidden, cfg.experts, cfg.shared_inter
+    b = distinct * per_expert_bytes(cfg) + E * H * 2 + 3 * Is * H * 2 + H * 2
+    if cfg.scoring == synth.SIGMOID_BIAS:
+        b += E * 4
+    b += rows * H * 2 * 4  # x, residual in; out, res_out out
+    return b
+
+
+class Workload:
+    """Device copies of one config's weights and rows, and a handle."""
+
+    def __init__(self, cfg, rows, copies, torch):
+        self.t = torch
+        self.cfg = cfg.with_rows(rows)
+        w = synth.make_weights(cfg)
+        rho = c2_rho() if cfg.similar else 0.0
+        x, r = synth.make_rows(self.cfg, rho=rho)
+        dev = lambda a: None if a is None else torch.from_numpy(
+            np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else np.ascontiguousarray(a)).cuda()
+        base = {k: dev(v) for k, v in w.items()}
+        del w
+        self.copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(copies - 1)]
+        self.x, self.r = dev(x), dev(r)
+        H = cfg.hidden
+        self.out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
+        self.res_out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
+        self.ids = torch.empty((rows, cfg.topk), dtype=torch.int32, device="cuda")
+        c = binding.make_config(rows, H, cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter, cfg.scoring, cfg.eps)
+        self.h = binding.MoeTail(c)
+        self.rows = rows
+
+    def call(self, i, stream, ids=False):
+        d = self.copies[i % len(self.copies)]
+        self.h.run(self.rows, self.x, self.r, d["gamma"], d["router_w"], d["router_bias"], d["w13_q"], d["w13_s"],
+                   d["w2_q"], d["w2_s"], d["ws13"], d["ws2"], self.out, self.res_out,
+                   self.ids if ids else None, None, stream=stream.cuda_stream)
+
+    def distinct(self, stream):
+        self.call(0, stream, ids=True)
+        stream.synchronize()
+        return len(set(self.ids.cpu().numpy().ravel().tolist()))
+
+    def time(self, steps, warmup, per_graph=50):
+        """µs per call over exactly `steps` calls (graph replays of `per_graph` calls)."""
+        t = self.t
+        s = t.cuda.Stream()
+        n_full, rem = divmod(steps, per_graph)
+        graphs = []
+        for n in ([per_graph] if n_full else []) + ([rem] if rem else []):
+            g = t.cuda.CUDAGraph()
+            with t.cuda.stream(s):
+                with t.cuda.graph(g, stream=s):
+                    for i in range(n):
+                        self.call(i, s)
+            graphs.append((n, g))
+        big = graphs[0][1]
+        for _ in range(max(1, warmup // per_graph)):
+            big.replay()
+        s.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(s)
+        with t.cuda.stream(s):
+            for _ in range(n_full):
+                graphs[0][1].replay()
+            if rem:
+                graphs[-1][1].replay()
+        e1.record(s)
+        s.synchronize()
+        if self.h.get_error() != binding.OK:
+            raise RuntimeError("device error during timing: " + binding.strerror(self.h.h))
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def time_eager(self, steps, warmup):
+        """µs per call over exactly `steps` direct launches (no graph), for profiler runs."""
+        t = self.t
+        s = t.cuda.Stream()
+        for i in range(warmup):
+            self.call(i, s)
+        s.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for i in range(steps):
+            self.call(i, s)
+        e1.record(s)
+        s.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def eager_us(self, reps=20):
+        t = self.t
+        s = t.cuda.Stream()
+        for i in range(3):
+            self.call(i, s)
+        s.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            self.call(i, s)
+            s.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / reps
+
+    def close(self):
+        self.h.close()
+        self.copies = None
+
+
+def copies_for(cfg, rows, distinct_guess):
+    b = alg_bytes(cfg, rows, distinct_guess)
+    return max(3, int(np.ceil(2 * MALL_BYTES / b)) + 1)
+
+
+def copy_bandwidth(torch):
+    """Device-to-device copy of a 2 GiB buffer: read + write GB/s (context for the peak)."""
+    n = 2**31
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbps
+
+
+def cpu_baseline(cfg, seconds=12.0):
+    """The oracle (single-threaded C, fp64) on full calls of the headline workload."""
+    import oracle  # test infrastructure: only this leg of the benchmark loads it
+
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg, rho=c2_rho() if cfg.similar else 0.0)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe_tail(x, r, w, cfg)
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": el * 1e6 / n, "unit": "µs per call", "cores": 1, "kind": "oracle",
+            "sample": "%d full %d-row calls of %s (%.1f s)" % (n, cfg.rows, cfg.name, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sweep", dest="sweep", action="store_true", default=True)
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-cpu", dest="cpu", action="store_false", default=True)
+    ap.add_argument("--only", default=None, help="time one workload only, e.g. c2 or c1:4")
+    ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
+    ap.add_argument("--calib", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (scale for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the tail (one tensor-parallel rank); "
+              "runs on more than one GPU are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    cfgs = synth.CONFIGS
+    if args.calib:
+        a = torch.ones(256 * 2**20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": a.numel(), "copies": 10}))
+        return
+
+    def measure(name, rows):
+        cfg = cfgs[name]
+        guess = {1: 10, 2: 20, 4: 39, 8: 56, 16: 139}.get(rows, rows * cfg.topk)
+        L = copies_for(cfg, rows, guess)
+        wl = Workload(cfg, rows, L, torch)
+        s = torch.cuda.Stream()
+        dist = wl.distinct(s)
+        us = wl.time_eager(args.steps, args.warmup) if args.eager else wl.time(args.steps, args.warmup)
+        B = alg_bytes(cfg, rows, dist)
+        rec = {"workload": name, "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
+               "us_per_call": round(us, 3), "GBps": round(B / (us * 1e-6) / 1e9, 1),
+               "frac_of_peak": round(B / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+        wl.close()
+        torch.cuda.empty_cache()
+        return rec
+
+    if args.only:
+        name, _, rows = args.only.partition(":")
+        measure(name, int(rows) if rows else cfgs[name].rows)
+        return
+
+    head = measure("c2", 8)
+    sweep = []
+    if args.sweep:
+        for rows in (1, 2, 4, 16):
+            sweep.append(measure("c1", rows))
+        sweep.append(head)
+        sweep.append(measure("c3", 4))
+        sweep.append(measure("c4", 16))
+    copy_gbps = copy_bandwidth(torch)
+    cpu = cpu_baseline(cfgs["c2"]) if args.cpu else None
+    us = head["us_per_call"]
+    line = {
+        "metric": METRIC,
+        "value": us,
+        "unit": "µs",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c2: one-rank decode shard, 8 rows, hidden 6144, 512 MXFP4 experts (E2M1, "
+                               "E8M0 block-32), top-10 softmax, I 256, bf16 shared Is 512, ~30% repeated picks",
+                   "rows": 8, "distinct_experts": head["distinct_experts"], "weight_copies": head["copies"]},
+        "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["frac_of_peak"], "traffic": None,
+                     "alg_bytes_per_call": head["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "copy_GBps": round(copy_gbps, 1),
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

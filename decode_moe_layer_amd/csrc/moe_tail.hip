@@ -3,7 +3,7 @@
 // Steps (one tensor-parallel rank's shard, 1..16 rows), after "[AMD]
 // integrate kimi k3 monokernel" (sglang PR 43481), K2 commit text, sections
 // Motivation and "Kernel Replacement":
-//   norm    h = bf16(x + residual); xn = bf16(h * rstd * gamma)
+//   norm    h = bf16(x + residual); xn = bf16(h * rstd * gamma), rstd in fp64
 //   router  logits = xn . Wr^T (fp32)
 //   top-k   K rounds of a wave-wide maximum, exact ties to the lower expert id
 //           ("glm53: Long-context indexer ...", PR 85 commit row 9)
@@ -12,9 +12,9 @@
 //   gate/up per (slot, 8 intermediate indices): 16 MFMA rows (8 gate + 8 up)
 //           against all using rows as MFMA columns; a = silu(g) * u
 //   shared  the bf16 shared expert's gate/up the same way
-//   down    per CTA a range of hidden rows: every slot's down tile and the
-//           shared down tile, products kept per (pick, row) in LDS
-//   combine y = sum over picks in slot order of w * d, plus the shared
+//   down    per workgroup a range of hidden rows: every slot's down tile and
+//           the shared down tile, products kept per (pick, row) in LDS
+//   combine y = sum over picks in (row, k) order of w * d, plus the shared
 //           output, in fp32 and a fixed order; out = bf16(h + y)
 //           (chunk-ordered fp32 partials: "Split the Kimi3 AttnRes mix across
 //           CTAs for decode rows", flare PR 11, design section)
@@ -26,12 +26,15 @@
 // deadline, a failed wait stops the launch everywhere).
 //
 // GEMV tiles use v_mfma_f32_16x16x32_bf16: weights are the A operand (16
-// rows), activations the B operand (up to 16 rows as columns).  MXFP4 codes
-// are dequantised exactly to bf16 with v_cvt_scalef32_pk_bf16_fp4 (E2M1 x
-// 2^(s-127) is exact in bf16 for the scales in range), so every product is
-// exact and accumulation is fp32.  A lane's 16-byte weight load is one whole
-// 32-element scale block (PR 85 commit row 18's 16-byte loads); weights are
-// read once per call with nontemporal loads (commit row 21).
+// rows), activations the B operand (up to 16 rows as columns), staged in LDS.
+// MXFP4 codes are dequantised exactly to bf16 with v_cvt_scalef32_pk_bf16_fp4
+// (E2M1 x 2^(s-127) is exact in bf16 for the scales in range), so every
+// product is exact and accumulation is fp32.  A lane's 16-byte weight load is
+// one whole 32-element scale block (PR 85 commit row 18's 16-byte loads);
+// weights are read once per call with nontemporal loads (commit row 21), and
+// each wave keeps a deep window of them in flight, issued ahead of the waits
+// they do not depend on (PR 85: weights are issued before an activation poll
+// is checked).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -39,6 +42,8 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "moe_tail.h"
 
@@ -51,8 +56,12 @@ constexpr int MAX_R = 16;
 constexpr int MAX_E = 512;
 constexpr int MAX_K = 32;
 constexpr int MAX_P = MAX_R * MAX_K;  // picks per call
-constexpr int MAX_BLK = 4;            // 16-row down blocks per workgroup
-constexpr int DEPTH = 4;              // loads in flight per wave in the streams
+constexpr int MAX_BLK = 2;            // 16-row down blocks per workgroup
+constexpr int D_BF = 12;              // bf16 weight loads in flight per wave
+constexpr int D_FP4 = 12;             // MXFP4 weight loads in flight per wave
+constexpr int D_FP4_G = 4;            // ... when activations come from global memory
+constexpr int D_DOWN = 8;             // down-projection items in flight per wave
+constexpr int XPAD = 8;               // bf16 padding per LDS activation row
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -76,13 +85,17 @@ struct Ctl {
   unsigned long long ticket;
   uint32_t _p0[62];
   uint32_t error;
-  uint32_t _p1[63];
+  uint32_t diag[7];  // first timeout: wait id, workgroup, observed, target, epoch, info
+  uint32_t _p1[56];
   Bank bank[2];
 };
 
 struct Params {
   int R, H, E, K, I, Is, scoring, G;
-  int shp_off;  // floats of the per-pick product area in dynamic LDS
+  int xn_lds;                     // activations staged in LDS (else read from global scratch)
+  int xs, as, ss;                 // LDS row strides (bf16 elements): xn, routed a, shared a
+  int off_as, off_outp, off_shp;  // byte offsets in dynamic LDS (down phase)
+  int xzero, azero, szero;        // indices of the all-zero LDS rows (inactive MFMA columns)
   double eps;
   unsigned long long deadline_ticks;
   uint32_t debug_flags;
@@ -114,9 +127,49 @@ struct Params {
 
 // ------------------------------------------------------------------ helpers --
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
-__device__ __forceinline__ uint32_t ld4(const void* p) { return *(const uint32_t*)p; }
+// Buffer accesses.  Weights use the default cache policy: an MFMA operand
+// load covers 64 bytes of each of 16 rows, so a 128-byte line is consumed by
+// two consecutive loads (and a line of block scales by eight), and a
+// nontemporal policy, which does not keep the line for the next load,
+// measured slower on MI355X (5.5 vs 6.3 TB/s for this pattern).
+// Out-of-range offsets read 0 without touching memory, which pads ragged
+// tiles and the tails of the load windows.  Exchanged scratch (xn, logits,
+// a) is written and read with device-scope (SC1) accesses, coherent across
+// the XCDs' L2s, so no L2 write-back or invalidate is ever needed.
+constexpr int CP_W = 0;
+constexpr int CP_SC1 = 16;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <int CP>
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP));
+}
+template <int CP>
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ uint32_t ld1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, CP);
+}
+__device__ __forceinline__ float ldcf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP_SC1));
+}
+__device__ __forceinline__ void stc16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
+                                         r, (int)off, 0, CP_SC1);
+}
+__device__ __forceinline__ void stcf(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, CP_SC1);
+}
+__device__ __forceinline__ void stc2(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, CP_SC1);
+}
+__device__ __forceinline__ u32x4 lds16(const void* p) { return *(const u32x4*)p; }
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -153,27 +206,63 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// monotone map of a float onto uint32 (larger float -> larger key); -0 == +0
+// monotone map of a float onto uint32 (larger float -> larger key); -0 == +0;
+// every finite key maps above 0, which marks a removed or absent expert
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+// Wave-wide reductions to lane 63 with DPP row shifts and row broadcasts,
+// read back as a uniform value.  Lanes without a DPP source take the identity.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ int dpp(int id, int v) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, RMASK, 0xF, false);
+}
+#define WAVE_REDUCE(v, OP, ID)                 \
+  v = OP(v, dpp<0x111, 0xF>((ID), (v)));       \
+  v = OP(v, dpp<0x112, 0xF>((ID), (v)));       \
+  v = OP(v, dpp<0x114, 0xF>((ID), (v)));       \
+  v = OP(v, dpp<0x118, 0xF>((ID), (v)));       \
+  v = OP(v, dpp<0x142, 0xA>((ID), (v)));       \
+  v = OP(v, dpp<0x143, 0xC>((ID), (v)));
+__device__ __forceinline__ int umax_(int a, int b) { return (uint32_t)a > (uint32_t)b ? a : b; }
+__device__ __forceinline__ int imin_(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int fadd_(int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  int v = (int)x;
+  WAVE_REDUCE(v, umax_, 0)
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_min_i32(int v) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  WAVE_REDUCE(v, imin_, 0x7FFFFFFF)
+  return __builtin_amdgcn_readlane(v, 63);
 }
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  int v = __float_as_int(x);
+  WAVE_REDUCE(v, fadd_, 0)
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = dpp<CTRL, RMASK>(0, __double2loint(v));
+  const int hi = dpp<CTRL, RMASK>(0, __double2hiint(v));
+  return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f64<0x111, 0xF>(v);
+  v += dpp_f64<0x112, 0xF>(v);
+  v += dpp_f64<0x114, 0xF>(v);
+  v += dpp_f64<0x118, 0xF>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                          __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int l = threadIdx.x & 63;
+  return l ? (~0ull >> (64 - l)) : 0ull;
 }
 
 // index of the n-th set bit of m (n < popcount(m))
@@ -182,41 +271,46 @@ __device__ __forceinline__ int nth_bit(uint32_t m, int n) {
   return __ffs(m) - 1;
 }
 
-// Rolling window over n items: item i's loads are issued DEPTH items before
-// it is consumed, so each wave keeps DEPTH loads in flight.
-template <class LoadF, class UseF>
-__device__ __forceinline__ void stream(int n, LoadF load, UseF use) {
-  using Frag = decltype(load(0));
-  if (n <= 0) return;
-  Frag buf[DEPTH];
+// A window of D loads in flight per wave.  `next()` issues the loads of the
+// next item of a source (items past the end read out of range, so every
+// step issues the same loads and the waits the compiler inserts stay exact);
+// `use` consumes items in order, D items behind the loads.
+template <int D, class Frag>
+struct Window {
+  Frag buf[D];
+  template <class NextF>
+  __device__ __forceinline__ void prime(NextF next) {
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) buf[j] = load(j < n ? j : n - 1);
-  for (int base = 0; base < n; base += DEPTH) {
+    for (int j = 0; j < D; ++j) buf[j] = next();
+  }
+  template <class NextF, class UseF>
+  __device__ __forceinline__ void run(int n, NextF next, UseF use) {
+    for (int base = 0; base < n; base += D) {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      const int i = base + j;
-      if (i < n) {
-        Frag cur = buf[j];
-        const int nx = i + DEPTH;
-        buf[j] = load(nx < n ? nx : n - 1);
-        use(cur, i);
+      for (int j = 0; j < D; ++j) {
+        if (base + j < n) {
+          Frag cur = buf[j];
+          buf[j] = next();
+          use(cur);
+        }
       }
     }
   }
-}
+};
 
 // -------------------------------------------------------- cross-CTA sync --
 
-// Make this workgroup's global writes visible at agent scope, then add n to *c.
+// Wait until this workgroup's (SC1) stores have completed, then add n to *c.
 __device__ __forceinline__ void publish(uint32_t* c, uint32_t n) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0 && n) __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroup-uniform wait for *c >= target with a deadline.  Returns false when
 // the launch is aborted (this wait timed out, or another one did).
-__device__ bool wait_ge(const Params& p, Bank* bk, uint32_t* c, uint32_t target, bool stall, uint32_t* s_flag) {
+__device__ __forceinline__ bool wait_ge(const Params& p, Bank* bk, uint32_t* c, uint32_t target, bool stall,
+                                        uint32_t* s_flag, uint32_t wait_id, uint32_t ep, uint32_t info) {
   if (threadIdx.x == 0) {
     uint32_t ok = 1;
     const unsigned long long t0 = wall_clock64();
@@ -229,44 +323,54 @@ __device__ bool wait_ge(const Params& p, Bank* bk, uint32_t* c, uint32_t target,
       }
       if (wall_clock64() - t0 > p.deadline_ticks) {
         __hip_atomic_store(&bk->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ctl->error, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t zero = 0;
+        if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          const uint32_t d[6] = {wait_id, blockIdx.x, v, target, ep, info};
+          for (int k = 0; k < 6; ++k)
+            __hip_atomic_store(&p.ctl->diag[k], d[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
     *s_flag = ok;
   }
   __syncthreads();
   const bool ok = *s_flag != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return ok;
 }
 
-// Workgroup-wide exclusive scan of one int per thread (threads >= n give 0).
-__device__ int block_exscan(int v, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  if (lane == 63) s_tmp[wave] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) base += s_tmp[w];
-    tot += s_tmp[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - v;
-}
+// Timeline build (-DMOE_TAIL_TIMELINE): thread 0 of every workgroup stamps
+// the 100 MHz real-time counter at each phase edge of the last call.
+#ifdef MOE_TAIL_TIMELINE
+constexpr int TL_N = 32;
+__device__ unsigned long long g_timeline[1024 * TL_N];
+#define TL(k)                                                                     \
+  do {                                                                            \
+    if (threadIdx.x == 0) g_timeline[blockIdx.x * TL_N + (k)] = wall_clock64(); \
+  } while (0)
+#define TL_ON 1
+#else
+#define TL(k) \
+  do {        \
+  } while (0)
+#define TL_ON 0
+#endif
 
-struct FragBF {
+struct FragA {  // one 16-byte weight load per lane
+  u32x4 a;
+};
+struct FragAB {  // weight + activation loads (activations from global scratch)
   u32x4 a, b;
 };
-struct FragFP4 {
+struct FragQ {  // MXFP4: codes + the 4 block scales of this instruction's chunks
+  u32x4 a;
+  uint32_t s;
+};
+struct FragQB {
   u32x4 a;
   uint32_t s;
   u32x4 b[4];
@@ -274,444 +378,684 @@ struct FragFP4 {
 struct FragDown {
   u32x4 a[MAX_BLK];
   uint32_t s[MAX_BLK];
-  u32x4 b[4];
 };
-struct FragSDown {
+struct FragSD {
   u32x4 a[MAX_BLK];
-  u32x4 b;
+};
+
+struct Shared {
+  uint32_t flags[8];
+  uint32_t ep;
+  double tmpd[NW];
+  int wcnt[NW];
+  int16_t ids[MAX_P];
+  float w[MAX_P];
+  int16_t ci[MAX_P];
+  int minpick[MAX_E];
+  uint32_t rowmask[MAX_E];
+  int16_t eslot[MAX_E];
+  int16_t slot_expert[MAX_P];
+  uint16_t slot_mask[MAX_P];
+  int16_t slot_off[MAX_P + 1];
+  int nslot;
+  f32x4 red[2][NW][64];
 };
 
 // ------------------------------------------------------------------ kernel --
 
-__global__ __launch_bounds__(NT, 1) void moe_tail_kernel(Params p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cta = blockIdx.x;
+template <bool XL>
+__device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
+  const int tid = threadIdx.x, lane = tid & 63, cta = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int R = p.R, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, G = p.G;
   const int P = R * K;
+  const int i16 = lane & 15, g = lane >> 4;  // MFMA row / column within 16, K-group
+  const rsrc_t rs_xn = make_rsrc(p.xn, (uint32_t)(R * H * 2));
+  const rsrc_t rs_lg = make_rsrc(p.logits, (uint32_t)(R * E * 4));
+  const rsrc_t rs_as = make_rsrc(p.a_s, (uint32_t)(R * Is * 2));
+  const rsrc_t rs_ar = make_rsrc(p.a_r, (uint32_t)(P * I * 2));
+  uint16_t* xl = (uint16_t*)dyn;  // [xrows][xs] staged activations; row xzero is zeros
+  const int xzero = p.xzero;
 
-  __shared__ uint32_t s_flags[8];
-  __shared__ uint32_t s_ep;
-  __shared__ double s_tmpd[NW];
-  __shared__ int s_tmpi[NW];
-  __shared__ int s_ids[MAX_P];
-  __shared__ float s_w[MAX_P];
-  __shared__ int s_ci[MAX_P];
-  __shared__ int s_minpick[MAX_E];
-  __shared__ uint32_t s_rowmask[MAX_E];
-  __shared__ int s_eslot[MAX_E];
-  __shared__ int s_slot_expert[MAX_P];
-  __shared__ uint32_t s_slot_mask[MAX_P];
-  __shared__ int s_slot_off[MAX_P + 1];
-  __shared__ int s_nslot;
-  __shared__ f32x4 s_red[2][NW][64];
-  extern __shared__ float s_dyn[];
-
-  // ---- epoch ticket: bank = ep & 1; workgroup 0 clears the next bank
-  if (tid == 0) {
-    const unsigned long long t = __hip_atomic_fetch_add(&p.ctl->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ep = (uint32_t)(t / (unsigned long long)G);
-  }
-  __syncthreads();
-  const uint32_t ep = s_ep;
-  Bank* bk = &p.ctl->bank[ep & 1];
-  if (cta == 0) {
-    uint32_t* nb = (uint32_t*)&p.ctl->bank[(ep + 1) & 1];
-    for (int i = tid; i < (int)(sizeof(Bank) / 4); i += NT) nb[i] = 0;
-  }
+  TL(0);
+  // ---- epoch ticket (its result is needed only at the first exchange)
+  unsigned long long tk = 0;
+  if (tid == 0) tk = __hip_atomic_fetch_add(&p.ctl->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool stall = (p.debug_flags & MOE_TAIL_DEBUG_STALL) && cta == p.debug_block;
 
+  // ---- P1 source: router row blocks (16 experts) then shared blocks (8 gate + 8 up);
+  // this workgroup's units are cta, cta + G, ...; wave w streams columns [t01, t01 + TP1) of 32
+  const int n_rb = (E + 15) / 16, n_sb = Is / 8, n_p1 = n_rb + n_sb;
+  const int T1 = H / 32, TP1 = (T1 + NW - 1) / NW, t01 = wave * TP1;
+  const int nu1 = cta < n_p1 ? (n_p1 - 1 - cta) / G + 1 : 0;
+  using P1Frag = typename std::conditional<XL, FragA, FragAB>::type;
+  Window<D_BF, P1Frag> w1;
+  int k1 = 0, t1 = t01;
+  bool r1 = true;
+  uint32_t roff1 = OOB;
+  rsrc_t rs1 = make_rsrc(p.rw, (uint32_t)((size_t)E * H * 2));
+  auto p1_unit = [&]() {  // decode unit k1
+    const int u = cta + k1 * G;
+    r1 = u < n_rb;
+    int row;
+    if (r1) {
+      row = u * 16 + i16 < E ? u * 16 + i16 : -1;
+      rs1 = make_rsrc(p.rw, (uint32_t)((size_t)E * H * 2));
+    } else {
+      const int sb = u - n_rb;
+      row = i16 < 8 ? sb * 8 + i16 : Is + sb * 8 + (i16 - 8);
+      rs1 = make_rsrc(p.ws13, (uint32_t)((size_t)2 * Is * H * 2));
+    }
+    roff1 = row >= 0 ? (uint32_t)(row * H + g * 8) * 2u : OOB;
+  };
+  if (nu1) p1_unit();
+  const uint32_t xoff = i16 < R ? (uint32_t)(i16 * H + g * 8) * 2u : OOB;
+  auto p1_next = [&]() {
+    P1Frag f;
+    const bool v = k1 < nu1 && t1 < T1;
+    f.a = ld16<CP_W>(rs1, (v && roff1 != OOB) ? roff1 + (uint32_t)t1 * 64u : OOB);
+    if constexpr (!XL) f.b = ld16<CP_SC1>(rs_xn, (v && xoff != OOB) ? xoff + (uint32_t)t1 * 64u : OOB);
+    if (++t1 == t01 + TP1) {
+      t1 = t01;
+      if (++k1 < nu1) p1_unit();
+    }
+    return f;
+  };
+  const bool is_norm = cta < R * NQ;
+  if constexpr (XL) {
+    if (!is_norm) w1.prime(p1_next);
+  }
+
   // ---- P0: fused residual add + RMSNorm; workgroup c < R*NQ owns a slice
-  if (cta < R * NQ) {
+  if (is_norm) {
     const int row = cta / NQ, q = cta % NQ;
-    const uint16_t* xr = p.x + (size_t)row * H;
-    const uint16_t* rr = p.res ? p.res + (size_t)row * H : nullptr;
+    const rsrc_t rx = make_rsrc(p.x + (size_t)row * H, (uint32_t)(H * 2));
+    const rsrc_t rr = make_rsrc(p.res ? p.res + (size_t)row * H : p.x, p.res ? (uint32_t)(H * 2) : 0u);
     double ss = 0.0;
-    for (int i = tid * 8; i < H; i += NT * 8) {
-      const u32x4 xv = ld16(xr + i);
-      const u32x4 rv = rr ? ld16(rr + i) : (u32x4){0u, 0u, 0u, 0u};
+    u32x4 xv[4], rv[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const double h0 = bf2f(f2bf(bf2f(xv[k] & 0xFFFFu) + bf2f(rv[k] & 0xFFFFu)));
-        const double h1 = bf2f(f2bf(bf2f(xv[k] >> 16) + bf2f(rv[k] >> 16)));
+    for (int k = 0; k < 4; ++k) {  // H <= 16384 = 4 x 512 x 8
+      const int i = (k * NT + tid) * 8;
+      xv[k] = ld16<0>(rx, i < H ? (uint32_t)i * 2u : OOB);
+      rv[k] = ld16<0>(rr, i < H ? (uint32_t)i * 2u : OOB);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double h0 = bf2f(f2bf(bf2f(xv[k][c] & 0xFFFFu) + bf2f(rv[k][c] & 0xFFFFu)));
+        const double h1 = bf2f(f2bf(bf2f(xv[k][c] >> 16) + bf2f(rv[k][c] >> 16)));
         ss = fma(h0, h0, ss);
         ss = fma(h1, h1, ss);
       }
     }
     ss = wave_sum_f64(ss);
-    if (lane == 0) s_tmpd[wave] = ss;
+    if (lane == 0) S.tmpd[wave] = ss;
     __syncthreads();
     double tot = 0.0;
-    for (int w = 0; w < NW; ++w) tot += s_tmpd[w];
+    for (int w = 0; w < NW; ++w) tot += S.tmpd[w];
     const double rstd = 1.0 / sqrt(tot / (double)H + p.eps);
-    const int SL = H / NQ, s0 = q * SL;
-    for (int i = s0 + tid * 8; i < s0 + SL; i += NT * 8) {
-      const u32x4 xv = ld16(xr + i);
-      const u32x4 rv = rr ? ld16(rr + i) : (u32x4){0u, 0u, 0u, 0u};
-      const u32x4 gv = ld16(p.gamma + i);
+    const int SL = H / NQ, i = q * SL + tid * 8;
+    if (tid * 8 < SL) {
+      const u32x4 x8 = ld16<0>(rx, (uint32_t)i * 2u);
+      const u32x4 r8 = ld16<0>(rr, (uint32_t)i * 2u);
+      const u32x4 g8 = *(const u32x4*)(p.gamma + i);
       u32x4 hv, nv;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t h0 = f2bf(bf2f(xv[k] & 0xFFFFu) + bf2f(rv[k] & 0xFFFFu));
-        const uint32_t h1 = f2bf(bf2f(xv[k] >> 16) + bf2f(rv[k] >> 16));
-        const uint32_t n0 = d2bf(((double)bf2f(h0) * rstd) * (double)bf2f(gv[k] & 0xFFFFu));
-        const uint32_t n1 = d2bf(((double)bf2f(h1) * rstd) * (double)bf2f(gv[k] >> 16));
-        hv[k] = h0 | (h1 << 16);
-        nv[k] = n0 | (n1 << 16);
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t h0 = f2bf(bf2f(x8[c] & 0xFFFFu) + bf2f(r8[c] & 0xFFFFu));
+        const uint32_t h1 = f2bf(bf2f(x8[c] >> 16) + bf2f(r8[c] >> 16));
+        const uint32_t n0 = d2bf(((double)bf2f(h0) * rstd) * (double)bf2f(g8[c] & 0xFFFFu));
+        const uint32_t n1 = d2bf(((double)bf2f(h1) * rstd) * (double)bf2f(g8[c] >> 16));
+        hv[c] = h0 | (h1 << 16);
+        nv[c] = n0 | (n1 << 16);
       }
-      *(u32x4*)(p.xn + (size_t)row * H + i) = nv;
+      stc16(rs_xn, (uint32_t)(row * H + i) * 2u, nv);
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
     }
-    publish(&bk->norm, 1);
   }
-  if (!wait_ge(p, bk, &bk->norm, (uint32_t)(R * NQ), stall, &s_flags[0])) return;
+  if (tid == 0) S.ep = (uint32_t)(tk / (unsigned long long)G);
+  __syncthreads();
+  const uint32_t ep = S.ep;
+  Bank* bk = &p.ctl->bank[ep & 1];
+  if (cta == 0) {  // the next call's bank, with write-through (SC1) stores:
+    // a dirty line left in this XCD's L2 could be written back over the
+    // next call's increments
+    uint32_t* nb = (uint32_t*)&p.ctl->bank[(ep + 1) & 1];
+    for (int i = tid; i < (int)(sizeof(Bank) / 4); i += NT)
+      __hip_atomic_store(nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (is_norm) publish(&bk->norm, 1);
+  if constexpr (XL) {
+    if (is_norm) w1.prime(p1_next);
+  }
+  TL(1);
+  if (!wait_ge(p, bk, &bk->norm, (uint32_t)(R * NQ), stall, &S.flags[0], 0, ep, 0)) return;
+  TL(2);
+  if constexpr (XL) {  // stage xn [R][H] -> LDS rows of stride xs; row xzero stays zero
+    const int n8 = R * H / 8;
+    for (int base = 0; base < n8; base += NT * 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        v[k] = ld16<CP_SC1>(rs_xn, e8 < n8 ? (uint32_t)e8 * 16u : OOB);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        if (e8 < n8) {
+          const int r = (e8 * 8) / H, c = (e8 * 8) % H;
+          *(u32x4*)(xl + r * p.xs + c) = v[k];
+        }
+      }
+    }
+    for (int c = tid * 8; c < p.xs; c += NT * 8) *(u32x4*)(xl + xzero * p.xs + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  } else {
+    w1.prime(p1_next);
+  }
+  TL(3);
 
   // ---- P1: router row blocks and shared gate/up blocks (waves split K)
-  const int n_rb = (E + 15) / 16, n_sb = Is / 8, n_p1 = n_rb + n_sb;
   {
-    const int T1 = H / 32, TP1 = (T1 + NW - 1) / NW;
-    const int t0 = min(T1, wave * TP1), t1 = min(T1, t0 + TP1);
-    const int i = lane & 15, g = lane >> 4, j = lane & 15;
-    uint32_t nr = 0, ns = 0;
-    for (int u = cta; u < n_p1; u += G) {
-      const bool is_router = u < n_rb;
-      const uint16_t* arow;
-      bool avalid = true;
-      if (is_router) {
-        const int e = u * 16 + i;
-        avalid = e < E;
-        arow = p.rw + (size_t)(avalid ? e : E - 1) * H;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int rb = 0, kk = 0, tt = 0;
+    const int brow = (i16 < R ? i16 : xzero) * p.xs + g * 8;  // this lane's activation row in LDS
+    w1.run(nu1 * TP1, p1_next, [&](const P1Frag& f) {
+      const int t = t01 + tt;
+      u32x4 b;
+      if constexpr (XL) {
+        b = lds16(xl + (t < T1 ? brow + t * 32 : xzero * p.xs));
       } else {
-        const int sb = u - n_rb;
-        arow = p.ws13 + (size_t)(i < 8 ? sb * 8 + i : Is + sb * 8 + (i - 8)) * H;
+        b = f.b;
       }
-      const bool bvalid = j < R;
-      const uint16_t* brow = p.xn + (size_t)(bvalid ? j : 0) * H;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      stream(
-          t1 - t0,
-          [&](int k) {
-            const int t = t0 + k;
-            FragBF f;
-            f.a = avalid ? ld16_nt(arow + t * 32 + g * 8) : (u32x4){0u, 0u, 0u, 0u};
-            f.b = bvalid ? ld16(brow + t * 32 + g * 8) : (u32x4){0u, 0u, 0u, 0u};
-            return f;
-          },
-          [&](const FragBF& f, int) { acc = mfma(as_bf16x8(f.a), as_bf16x8(f.b), acc); });
-      s_red[0][wave][lane] = acc;
-      __syncthreads();
-      if (is_router) {
-        if (tid < 256) {
-          const int l = tid >> 2, qq = tid & 3;
-          float v = 0.f;
-          for (int w = 0; w < NW; ++w) v += s_red[0][w][l][qq];
-          const int e = u * 16 + 4 * (l >> 4) + qq, col = l & 15;
-          if (e < E && col < R) p.logits[(size_t)col * E + e] = v;
-        }
-        ++nr;
-      } else {
-        if (tid < 128) {
-          const int l = tid >> 2, qq = tid & 3;
-          float gsum = 0.f, usum = 0.f;
-          for (int w = 0; w < NW; ++w) {
-            gsum += s_red[0][w][l][qq];
-            usum += s_red[0][w][l + 32][qq];
+      acc = mfma(as_bf16x8(f.a), as_bf16x8(b), acc);
+      if (++tt == TP1) {  // unit done: reduce the 8 waves' partials in wave order
+        tt = 0;
+        const int u = cta + kk * G;
+        ++kk;
+        S.red[rb][wave][lane] = acc;
+        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (u < n_rb) {
+          if (tid < 256) {
+            const int l = tid >> 2, qq = tid & 3;
+            float v = 0.f;
+            for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
+            const int e = u * 16 + 4 * (l >> 4) + qq, col = l & 15;
+            if (e < E && col < R) stcf(rs_lg, (uint32_t)(col * E + e) * 4u, v);
           }
-          const int ii = 4 * (l >> 4) + qq, col = l & 15;
-          const float a = gsum / (1.f + __expf(-gsum)) * usum;
-          if (col < R) p.a_s[(size_t)col * Is + (u - n_rb) * 8 + ii] = (uint16_t)f2bf(a);
+        } else {
+          if (tid < 128) {
+            const int l = tid >> 2, qq = tid & 3;
+            float gs = 0.f, us = 0.f;
+            for (int w = 0; w < NW; ++w) {
+              gs += S.red[rb][w][l][qq];
+              us += S.red[rb][w][l + 32][qq];
+            }
+            const int ii = 4 * (l >> 4) + qq, col = l & 15;
+            const float a = gs / (1.f + __expf(-gs)) * us;
+            if (col < R) stc2(rs_as, (uint32_t)(col * Is + (u - n_rb) * 8 + ii) * 2u, f2bf(a));
+          }
         }
-        ++ns;
+        rb ^= 1;
       }
-      __syncthreads();
-    }
+    });
+    // this workgroup's units are cta, cta + G, ...: the first nr are router blocks
+    const uint32_t nr = cta < n_rb ? (uint32_t)((n_rb - 1 - cta) / G + 1) : 0u;
+    const uint32_t ns = (uint32_t)nu1 - nr;
     if (nr) publish(&bk->router, nr);
     if (ns) publish(&bk->shared, ns);
   }
+  TL(4);
 
   // ---- top-k on every workgroup (identical inputs, identical result)
-  if (!wait_ge(p, bk, &bk->router, (uint32_t)n_rb, false, &s_flags[1])) return;
+  if (!wait_ge(p, bk, &bk->router, (uint32_t)n_rb, false, &S.flags[1], 1, ep, 0)) return;
+  TL(5);
   for (int r = wave; r < R; r += NW) {
     uint32_t key[8];
     float lg[8];
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const int e = lane + 64 * v;
-      if (e < E) {
-        const float l = p.logits[(size_t)r * E + e];
-        lg[v] = l;
-        const float kf = p.scoring == MOE_TAIL_SOFTMAX ? l : 1.f / (1.f + __expf(-l)) + p.bias[e];
-        key[v] = ord_key(kf);
-      } else {
-        lg[v] = 0.f;
-        key[v] = 0u;
-      }
+      const float l = ldcf(rs_lg, e < E ? (uint32_t)(r * E + e) * 4u : OOB);
+      lg[v] = l;
+      const float kf = p.scoring == MOE_TAIL_SOFTMAX ? l : 1.f / (1.f + __expf(-l)) + (e < E ? p.bias[e] : 0.f);
+      key[v] = e < E ? ord_key(kf) : 0u;
     }
-    for (int k = 0; k < K; ++k) {
-      uint32_t bkey = key[0];
-      int bv = 0;
+    uint32_t lmax = key[0];
+    int lslot = 0;
 #pragma unroll
-      for (int v = 1; v < 8; ++v)
-        if (key[v] > bkey) {
-          bkey = key[v];
-          bv = v;
-        }
-      const uint32_t m = wave_max_u32(bkey);
-      const unsigned long long bal = __ballot(bkey == m);
+    for (int v = 1; v < 8; ++v)
+      if (key[v] > lmax) {
+        lmax = key[v];
+        lslot = v;
+      }
+    for (int k = 0; k < K; ++k) {
+      const uint32_t m = wave_max_u32(lmax);
+      const uint64_t bal = __ballot(lmax == m);
       int id;
       if (__popcll(bal) == 1) {
-        id = __shfl(lane + 64 * bv, __ffsll((long long)bal) - 1);
-      } else {
-        id = wave_min_i32(bkey == m ? lane + 64 * bv : 0x7FFFFFFF);
+        const int wl = __ffsll((unsigned long long)bal) - 1;
+        id = wl + 64 * __builtin_amdgcn_readlane(lslot, wl);
+      } else {  // exact tie: the lowest expert id among the tied lanes
+        id = wave_min_i32(lmax == m ? lane + 64 * lslot : 0x7FFFFFFF);
       }
       float lsel = 0.f;
+      if (lane == (id & 63)) {
 #pragma unroll
-      for (int v = 0; v < 8; ++v)
-        if (lane == (id & 63) && v == (id >> 6)) {
-          key[v] = 0u;
-          lsel = lg[v];
-        }
-      lsel = __shfl(lsel, id & 63);
+        for (int v = 0; v < 8; ++v)
+          if (v == (id >> 6)) {
+            key[v] = 0u;
+            lsel = lg[v];
+          }
+        lmax = key[0];
+        lslot = 0;
+#pragma unroll
+        for (int v = 1; v < 8; ++v)
+          if (key[v] > lmax) {
+            lmax = key[v];
+            lslot = v;
+          }
+      }
+      lsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsel), id & 63));
       if (lane == 0) {
-        s_ids[r * K + k] = id;
-        s_w[r * K + k] = lsel;
+        S.ids[r * K + k] = (int16_t)id;
+        S.w[r * K + k] = lsel;
       }
     }
-    // normalised weights over the K picks (lanes k < K)
-    const float l0 = s_w[r * K];
+    // normalised weights over the K picks (lanes k < K); S.w holds the logits
+    const float l0 = S.w[r * K];
     float t = 0.f;
     if (lane < K) {
-      const float l = s_w[r * K + lane];
+      const float l = S.w[r * K + lane];
       t = p.scoring == MOE_TAIL_SOFTMAX ? __expf(l - l0) : 1.f / (1.f + __expf(-l));
     }
     const float sum = wave_sum_f32(t);
-    if (lane < K) s_w[r * K + lane] = t / sum;
+    if (lane < K) S.w[r * K + lane] = t / sum;
   }
+  TL(6);
 
   // ---- de-duplication: slot = distinct expert, in order of first pick
   for (int e = tid; e < E; e += NT) {
-    s_minpick[e] = 0x7FFFFFFF;
-    s_rowmask[e] = 0u;
+    S.minpick[e] = 0x7FFFFFFF;
+    S.rowmask[e] = 0u;
   }
   __syncthreads();
-  for (int q = tid; q < P; q += NT) {
-    atomicMin(&s_minpick[s_ids[q]], q);
-    atomicOr(&s_rowmask[s_ids[q]], 1u << (q / K));
+  if (tid < P) {
+    atomicMin(&S.minpick[S.ids[tid]], tid);
+    atomicOr(&S.rowmask[S.ids[tid]], 1u << (tid / K));
   }
   __syncthreads();
   {
-    const bool first = tid < P && s_minpick[s_ids[tid]] == tid;
-    int nslot;
-    const int slot = block_exscan(first ? 1 : 0, s_tmpi, &nslot);
-    if (first) {
-      const int e = s_ids[tid];
-      s_eslot[e] = slot;
-      s_slot_expert[slot] = e;
-      s_slot_mask[slot] = s_rowmask[e];
-    }
-    if (tid == 0) s_nslot = nslot;
+    const bool first = tid < P && S.minpick[S.ids[tid]] == tid;
+    const uint64_t bal = __ballot(first);
+    if (lane == 0) S.wcnt[wave] = __popcll(bal);
     __syncthreads();
-    const int m = tid < nslot ? __popc(s_slot_mask[tid]) : 0;
-    int tot;
-    const int off = block_exscan(m, s_tmpi, &tot);
-    if (tid < nslot) s_slot_off[tid] = off;
-    if (tid == 0) s_slot_off[nslot] = tot;
+    int base = 0, nslot = 0;
+    for (int w = 0; w < NW; ++w) {
+      base += w < wave ? S.wcnt[w] : 0;
+      nslot += S.wcnt[w];
+    }
+    const int slot = base + __popcll(bal & lanes_below());
+    if (first) {
+      const int e = S.ids[tid];
+      S.eslot[e] = (int16_t)slot;
+      S.slot_expert[slot] = (int16_t)e;
+      S.slot_mask[slot] = (uint16_t)S.rowmask[e];
+    }
+    __syncthreads();
+    // exclusive prefix over slots of the user count m_d (<= 16): bitwise ballots
+    const int m = tid < nslot ? __popc((uint32_t)S.slot_mask[tid]) : 0;
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+      const uint64_t bb = __ballot((m >> b) & 1);
+      pre += __popcll(bb & lanes_below()) << b;
+      tot += __popcll(bb) << b;
+    }
+    if (lane == 0) S.wcnt[wave] = tot;
+    __syncthreads();
+    int off = pre, all = 0;
+    for (int w = 0; w < NW; ++w) {
+      off += w < wave ? S.wcnt[w] : 0;
+      all += S.wcnt[w];
+    }
+    if (tid < nslot) S.slot_off[tid] = (int16_t)off;
+    if (tid == 0) {
+      S.slot_off[nslot] = (int16_t)all;
+      S.nslot = nslot;
+    }
     __syncthreads();
     if (tid < P) {
-      const int e = s_ids[tid], d = s_eslot[e], r = tid / K;
-      s_ci[tid] = s_slot_off[d] + __popc(s_slot_mask[d] & ((1u << r) - 1u));
+      const int d = S.eslot[S.ids[tid]], r = tid / K;
+      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
     }
     __syncthreads();
   }
-  const int D = s_nslot;
+  const int D = S.nslot;
   if (cta == 0) {
     for (int q = tid; q < P; q += NT) {
-      if (p.topk_ids) p.topk_ids[q] = s_ids[q];
-      if (p.topk_w) p.topk_w[q] = s_w[q];
+      if (p.topk_ids) p.topk_ids[q] = S.ids[q];
+      if (p.topk_w) p.topk_w[q] = S.w[q];
     }
     if (p.dbg_logits)
-      for (int q = tid; q < R * E; q += NT) p.dbg_logits[q] = p.logits[q];
+      for (int q = tid; q < R * E; q += NT) p.dbg_logits[q] = ldcf(rs_lg, (uint32_t)q * 4u);
   }
+  TL(7);
 
-  // ---- P2: routed gate/up units (slot, 8 intermediate indices)
-  const int UB = I / 8, n_p2 = D * UB;
+  // ---- P2: routed gate/up units (slot, 8 intermediate indices), waves split K
   {
-    const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW;
-    const int t0 = min(T2, wave * TP2), t1 = min(T2, t0 + TP2);
-    const int i = lane & 15, g = lane >> 4, j = lane & 15;
-    const int off = n_p1 % G;
-    uint32_t nu = 0;
-    int buf = 0;
-    for (int u = (cta - off + G) % G; u < n_p2; u += G, buf ^= 1) {
-      const int d = u / UB, b = u % UB;
-      const int e = s_slot_expert[d];
-      const uint32_t mask = s_slot_mask[d];
-      const int m = __popc(mask), ci0 = s_slot_off[d];
-      const int wrow = i < 8 ? b * 8 + i : I + b * 8 + (i - 8);
-      const uint8_t* arow = p.w13q + ((size_t)e * 2 * I + wrow) * (size_t)(H / 2);
-      const uint8_t* srow = p.w13s + ((size_t)e * 2 * I + wrow) * (size_t)(H / 32);
-      const bool bvalid = j < m;
-      const uint16_t* brow = p.xn + (size_t)(bvalid ? nth_bit(mask, j) : 0) * H;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      stream(
-          t1 - t0,
-          [&](int k) {
-            const int t = t0 + k, c = 4 * t + g;
-            FragFP4 f;
-            f.a = ld16_nt(arow + c * 16);
-            f.s = ld4(srow + 4 * t);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              f.b[q] = bvalid ? ld16(brow + c * 32 + 8 * q) : (u32x4){0u, 0u, 0u, 0u};
-            return f;
-          },
-          [&](const FragFP4& f, int) {
-            const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[q], sc), as_bf16x8(f.b[q]), acc);
-          });
-      s_red[buf][wave][lane] = acc;
-      __syncthreads();
-      if (tid < 128) {
-        const int l = tid >> 2, qq = tid & 3;
-        float gsum = 0.f, usum = 0.f;
-        for (int w = 0; w < NW; ++w) {
-          gsum += s_red[buf][w][l][qq];
-          usum += s_red[buf][w][l + 32][qq];
-        }
-        const int ii = 4 * (l >> 4) + qq, col = l & 15;
-        const float a = gsum / (1.f + __expf(-gsum)) * usum;
-        if (col < m) p.a_r[(size_t)(ci0 + col) * I + b * 8 + ii] = (uint16_t)f2bf(a);
+    const int UB = I / 8, n_p2 = D * UB;
+    const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW, t02 = wave * TP2;
+    const int u0 = (cta - n_p1 % G + G) % G;
+    const int nu2 = u0 < n_p2 ? (n_p2 - 1 - u0) / G + 1 : 0;
+    const size_t S13 = (size_t)2 * I * (H / 2), S13s = (size_t)2 * I * (H / 32);
+    using P2Frag = typename std::conditional<XL, FragQ, FragQB>::type;
+    // source cursor: unit k2, column group t2
+    int k2 = 0, t2 = t02;
+    rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
+    uint32_t qoff = 0, soff = 0, boff = OOB;
+    auto p2_unit = [&]() {
+      const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
+      const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
+      rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
+      rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
+      const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
+      qoff = (uint32_t)(wrow * (H / 2) + g * 16);
+      soff = (uint32_t)(wrow * (H / 32));
+      if constexpr (!XL) {
+        const uint32_t mask = S.slot_mask[d];
+        boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
       }
-      ++nu;
-    }
-    if (nu) publish(&bk->routed, nu);
+    };
+    if (nu2) p2_unit();
+    auto p2_next = [&]() {
+      P2Frag f;
+      const bool v = k2 < nu2 && t2 < T2;
+      f.a = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * 64u : OOB);
+      f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
+      if constexpr (!XL) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          f.b[q] = ld16<CP_SC1>(rs_xn, (v && boff != OOB) ? boff + (uint32_t)(t2 * 256 + 16 * q) : OOB);
+      }
+      if (++t2 == t02 + TP2) {
+        t2 = t02;
+        if (++k2 < nu2) p2_unit();
+      }
+      return f;
+    };
+    Window<XL ? D_FP4 : D_FP4_G, P2Frag> w2;
+    w2.prime(p2_next);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int rb = 0, kk = 0, tt = 0, brow = 0, d = 0, m = 0;
+    auto p2_user = [&]() {  // consumer side of unit kk
+      const int u = u0 + kk * G;
+      d = u / UB;
+      const uint32_t mask = S.slot_mask[d];
+      m = __popc(mask);
+      brow = (i16 < m ? nth_bit(mask, i16) : xzero) * p.xs + g * 32;
+    };
+    if (nu2) p2_user();
+    if (nu2 && TL_ON) TL(13);
+    w2.run(nu2 * TP2, p2_next, [&](const P2Frag& f) {
+      const int t = t02 + tt;
+      const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
+      u32x4 b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (XL) {
+          b[q] = lds16(xl + (t < T2 ? brow + t * 128 + 8 * q : xzero * p.xs));
+        } else {
+          b[q] = f.b[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[q], sc), as_bf16x8(b[q]), acc);
+      if (++tt == TP2) {
+        tt = 0;
+        const int u = u0 + kk * G, bb = u - d * UB;
+        S.red[rb][wave][lane] = acc;
+        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (tid < 128) {
+          const int l = tid >> 2, qq = tid & 3;
+          float gs = 0.f, us = 0.f;
+          for (int w = 0; w < NW; ++w) {
+            gs += S.red[rb][w][l][qq];
+            us += S.red[rb][w][l + 32][qq];
+          }
+          const int ii = 4 * (l >> 4) + qq, col = l & 15;
+          const float a = gs / (1.f + __expf(-gs)) * us;
+          if (col < m) stc2(rs_ar, (uint32_t)((S.slot_off[d] + col) * I + bb * 8 + ii) * 2u, f2bf(a));
+        }
+        if (kk < 12) TL(14 + kk);
+        rb ^= 1;
+        if (++kk < nu2) p2_user();
+      }
+    });
+    if (nu2) publish(&bk->routed, (uint32_t)nu2);
   }
+  TL(8);
 
   // ---- P3: down projections for this workgroup's hidden rows, then combine
-  if (Is > 0 && !wait_ge(p, bk, &bk->shared, (uint32_t)n_sb, false, &s_flags[2])) return;
-  if (!wait_ge(p, bk, &bk->routed, (uint32_t)n_p2, false, &s_flags[3])) return;
   const int HR = (H + G - 1) / G;
   const int h0 = cta * HR, hn = max(0, min(H, h0 + HR) - h0);
-  if (hn == 0) return;
   const int nblk = (hn + 15) / 16;
-  float* s_outp = s_dyn;                             // [P][HR]
-  float* s_shp = s_dyn + p.shp_off;                  // [NW][R][HR]
-  {
-    const int i = lane & 15, g = lane >> 4, j = lane & 15;
-    // shared down: waves split the Is/32 chunks
-    if (Is > 0) {
-      const int Cs = Is / 32, CP = (Cs + NW - 1) / NW;
-      const int c0 = min(Cs, wave * CP), c1 = min(Cs, c0 + CP);
-      const bool bvalid = j < R;
-      f32x4 acc[MAX_BLK];
+  const int CI = I / 32, TI = (CI + 3) / 4;
+  const int nsl = D > wave ? (D - wave + NW - 1) / NW : 0;
+  const size_t S2 = (size_t)H * (I / 2), S2s = (size_t)H * CI;
+  uint16_t* al = (uint16_t*)dyn;                // [P + 1][as] routed a; row azero is zeros
+  uint16_t* asl = (uint16_t*)(dyn + p.off_as);  // [R + 1][ss] shared a; row szero is zeros
+  float* s_outp = (float*)(dyn + p.off_outp);   // [P][HR]
+  float* s_shp = (float*)(dyn + p.off_shp);     // [NW][R][HR]
+  const int azero = p.azero, szero = p.szero;
+  // source cursor: slot j3 (slot d = wave + NW * j3), column group t3
+  int j3 = 0, t3 = 0;
+  rsrc_t rq3 = rs_xn, rsc3 = rs_xn;
+  auto p3_slot = [&]() {
+    const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]);  // uniform: scalar descriptors
+    rq3 = make_rsrc(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
+    rsc3 = make_rsrc(p.w2s + e * S2s + (size_t)h0 * CI, (uint32_t)(hn * CI));
+  };
+  if (nsl && hn) p3_slot();
+  auto p3_next = [&]() {
+    FragDown f;
+    const int c = 4 * t3 + g;
+    const bool v = j3 < nsl && hn > 0 && c < CI;
 #pragma unroll
-      for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      stream(
-          c1 - c0,
-          [&](int k) {
-            const int c = c0 + k;
-            FragSDown f;
+    for (int bl = 0; bl < MAX_BLK; ++bl) {
+      const int hh = 16 * bl + i16;
+      const bool vv = v && bl < nblk && hh < hn;
+      f.a[bl] = ld16<CP_W>(rq3, vv ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
+      f.s[bl] = ld1<CP_W>(rsc3, vv ? (uint32_t)(hh * CI + c) : OOB);
+    }
+    if (++t3 == TI) {
+      t3 = 0;
+      if (++j3 < nsl && hn) p3_slot();
+    }
+    return f;
+  };
+  Window<D_DOWN, FragDown> w3;
+  w3.prime(p3_next);
+  TL(9);
+  if (Is > 0 && !wait_ge(p, bk, &bk->shared, (uint32_t)n_sb, false, &S.flags[2], 2, ep, (uint32_t)D)) return;
+  if (!wait_ge(p, bk, &bk->routed, (uint32_t)(D * (I / 8)), false, &S.flags[3], 3, ep, (uint32_t)D)) return;
+  if (hn == 0) return;
+  TL(10);
+  {  // stage the routed a [P][I] and the shared a [R][Is] into LDS, plus their zero rows
+    const int nr8 = P * I / 8, ns8 = R * Is / 8, n8 = nr8 + ns8;
+    for (int base = 0; base < n8; base += NT * 4) {
+      u32x4 v[4];
 #pragma unroll
-            for (int bl = 0; bl < MAX_BLK; ++bl) {
-              const int hh = 16 * bl + i;
-              f.a[bl] = (bl < nblk && hh < hn) ? ld16_nt(p.ws2 + (size_t)(h0 + hh) * Is + c * 32 + g * 8)
-                                               : (u32x4){0u, 0u, 0u, 0u};
-            }
-            f.b = bvalid ? ld16(p.a_s + (size_t)j * Is + c * 32 + g * 8) : (u32x4){0u, 0u, 0u, 0u};
-            return f;
-          },
-          [&](const FragSDown& f, int) {
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        v[k] = e8 < nr8 ? ld16<CP_SC1>(rs_ar, (uint32_t)e8 * 16u)
+                        : ld16<CP_SC1>(rs_as, e8 < n8 ? (uint32_t)(e8 - nr8) * 16u : OOB);
+      }
 #pragma unroll
-            for (int bl = 0; bl < MAX_BLK; ++bl)
-              if (bl < nblk) acc[bl] = mfma(as_bf16x8(f.a[bl]), as_bf16x8(f.b), acc[bl]);
-          });
-#pragma unroll
-      for (int bl = 0; bl < MAX_BLK; ++bl) {
-        if (bl >= nblk) break;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int hh = 16 * bl + 4 * g + qq;
-          if (hh < hn && j < R) s_shp[((size_t)wave * R + j) * HR + hh] = acc[bl][qq];
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        if (e8 < nr8) {
+          *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+        } else if (e8 < n8) {
+          const int s8 = e8 - nr8;
+          *(u32x4*)(asl + ((s8 * 8) / Is) * p.ss + (s8 * 8) % Is) = v[k];
         }
       }
     }
-    // routed down: slot d on wave d % NW; items (slot, t) with t over I/128
-    const int CI = I / 32, TI = (CI + 3) / 4;
-    const int nsl = D > wave ? (D - wave + NW - 1) / NW : 0;
+    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
+    for (int c = tid * 8; c < p.ss; c += NT * 8) *(u32x4*)(asl + szero * p.ss + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  // shared down: waves split the Is/32 chunks
+  if (Is > 0) {
+    const int Cs = Is / 32, CP = (Cs + NW - 1) / NW, c0 = wave * CP;
+    const rsrc_t rq = make_rsrc(p.ws2 + (size_t)h0 * Is, (uint32_t)(hn * Is * 2));
     f32x4 acc[MAX_BLK];
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    stream(
-        nsl * TI,
-        [&](int k) {
-          const int d = wave + NW * (k / TI), t = k % TI, c = 4 * t + g;
-          const int e = s_slot_expert[d];
-          const int m = __popc(s_slot_mask[d]), ci0 = s_slot_off[d];
-          const bool cvalid = c < CI;
-          FragDown f;
+    Window<4, FragSD> ws;
+    int cs = c0, cu = c0;
+    auto sd_next = [&]() {
+      FragSD f;
 #pragma unroll
-          for (int bl = 0; bl < MAX_BLK; ++bl) {
-            const int hh = 16 * bl + i;
-            const bool v = bl < nblk && hh < hn && cvalid;
-            const size_t rowi = (size_t)e * H + (size_t)(h0 + (v ? hh : 0));
-            f.a[bl] = v ? ld16_nt(p.w2q + rowi * (I / 2) + c * 16) : (u32x4){0u, 0u, 0u, 0u};
-            f.s[bl] = v ? (uint32_t)p.w2s[rowi * CI + c] : 127u;
-          }
+      for (int bl = 0; bl < MAX_BLK; ++bl) {
+        const int hh = 16 * bl + i16;
+        f.a[bl] = ld16<CP_W>(rq, (cs < c0 + CP && cs < Cs && bl < nblk && hh < hn) ? (uint32_t)(hh * Is + cs * 32 + g * 8) * 2u : OOB);
+      }
+      ++cs;
+      return f;
+    };
+    const int srow = (i16 < R ? i16 : szero) * p.ss + g * 8;
+    ws.prime(sd_next);
+    ws.run(CP, sd_next, [&](const FragSD& f) {
+      const u32x4 b = lds16(asl + (cu < Cs ? srow + cu * 32 : szero * p.ss));
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            f.b[q] = (j < m && cvalid) ? ld16(p.a_r + (size_t)(ci0 + j) * I + c * 32 + 8 * q) : (u32x4){0u, 0u, 0u, 0u};
-          return f;
-        },
-        [&](const FragDown& f, int k) {
+      for (int bl = 0; bl < MAX_BLK; ++bl)
+        if (bl < nblk) acc[bl] = mfma(as_bf16x8(f.a[bl]), as_bf16x8(b), acc[bl]);
+      ++cu;
+    });
 #pragma unroll
-          for (int bl = 0; bl < MAX_BLK; ++bl) {
-            if (bl < nblk) {
-              const float sc = e8m0f(f.s[bl]);
+    for (int bl = 0; bl < MAX_BLK; ++bl) {
+      if (bl < nblk) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[bl][q], sc), as_bf16x8(f.b[q]), acc[bl]);
-            }
-          }
-          if (k % TI == TI - 1) {
-            const int d = wave + NW * (k / TI);
-            const int m = __popc(s_slot_mask[d]), ci0 = s_slot_off[d];
-#pragma unroll
-            for (int bl = 0; bl < MAX_BLK; ++bl) {
-              if (bl < nblk) {
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                  const int hh = 16 * bl + 4 * g + qq;
-                  if (hh < hn && j < m) s_outp[(size_t)(ci0 + j) * HR + hh] = acc[bl][qq];
-                }
-              }
-              acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-          }
-        });
+        for (int qq = 0; qq < 4; ++qq) {
+          const int hh = 16 * bl + 4 * g + qq;
+          if (hh < hn && i16 < R) s_shp[(wave * R + i16) * HR + hh] = acc[bl][qq];
+        }
+      }
+    }
   }
+  // routed down: slot d on wave d % NW; items (slot, t) with t over I/128
+  {
+    f32x4 acc[MAX_BLK];
+#pragma unroll
+    for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    int ju = 0, tu = 0, m = 0, ci0 = 0, arow = 0;
+    auto p3_user = [&]() {
+      const int d = wave + NW * ju;
+      m = __popc((uint32_t)S.slot_mask[d]);
+      ci0 = S.slot_off[d];
+      arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
+    };
+    if (nsl) p3_user();
+    w3.run(nsl * TI, p3_next, [&](const FragDown& f) {
+      const int c = 4 * tu + g;
+      u32x4 b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + tu * 128 + 8 * q : azero * p.as));
+#pragma unroll
+      for (int bl = 0; bl < MAX_BLK; ++bl) {
+        if (bl < nblk) {
+          const float sc = e8m0f(f.s[bl] & 0xFFu);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[bl][q], sc), as_bf16x8(b[q]), acc[bl]);
+        }
+      }
+      if (++tu == TI) {
+        tu = 0;
+#pragma unroll
+        for (int bl = 0; bl < MAX_BLK; ++bl) {
+          if (bl < nblk) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int hh = 16 * bl + 4 * g + qq;
+              if (hh < hn && i16 < m) s_outp[(ci0 + i16) * HR + hh] = acc[bl][qq];
+            }
+          }
+          acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        if (++ju < nsl) p3_user();
+      }
+    });
+  }
+  TL(11);
   __syncthreads();
   // combine in a fixed order: picks in (row, k) order, then the shared part
   for (int idx = tid; idx < R * hn; idx += NT) {
     const int r = idx / hn, hh = idx % hn, h = h0 + hh;
     float yr = 0.f;
-    for (int k = 0; k < K; ++k) yr += s_w[r * K + k] * s_outp[(size_t)s_ci[r * K + k] * HR + hh];
+    for (int k = 0; k < K; ++k) yr += S.w[r * K + k] * s_outp[S.ci[r * K + k] * HR + hh];
     float ys = 0.f;
     if (Is > 0)
-      for (int w = 0; w < NW; ++w) ys += s_shp[((size_t)w * R + r) * HR + hh];
+      for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
     const uint32_t hb = f2bf(bf2f(p.x[(size_t)r * H + h]) + (p.res ? bf2f(p.res[(size_t)r * H + h]) : 0.f));
     p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
     if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
     if (p.dbg_ys) p.dbg_ys[(size_t)r * H + h] = ys;
   }
+  TL(12);
+}
+
+__global__ __launch_bounds__(NT, 1) void moe_tail_kernel(Params p) {
+  __shared__ Shared S;
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  if (p.xn_lds)
+    tail<true>(p, S, s_dyn);
+  else
+    tail<false>(p, S, s_dyn);
 }
 
 }  // namespace mt
 
 // ==================================================================== host ==
 
+// Dynamic LDS plan.  The gate/up phases stage xn [rows][H + pad] when it
+// fits; the down phase (which reuses the same space) stages the routed a
+// [picks][I + pad], the shared a [rows][Is + pad], the per-pick products
+// [picks][HR] and the shared partials [waves][rows][HR].
+struct LdsPlan {
+  int xn_lds, xs, as, ss, off_as, off_outp, off_shp;
+  size_t down, xn, dyn;
+};
+
+static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+static LdsPlan lds_plan(const moe_tail_config* c, int G, size_t static_bytes, size_t limit) {
+  LdsPlan L;
+  const size_t R = c->max_rows, P = (size_t)c->max_rows * c->top_k, HR = (size_t)(c->hidden + G - 1) / G;
+  L.xs = c->hidden + mt::XPAD;
+  L.as = c->inter + mt::XPAD;
+  L.ss = c->shared_inter + mt::XPAD;
+  L.off_as = (int)al16((P + 1) * L.as * 2);
+  L.off_outp = (int)(L.off_as + al16((R + 1) * L.ss * 2));
+  L.off_shp = (int)(L.off_outp + al16(P * HR * 4));
+  L.down = L.off_shp + al16((size_t)mt::NW * R * HR * 4);
+  L.xn = (R + 1) * (size_t)L.xs * 2;
+  L.xn_lds = static_bytes + (L.xn > L.down ? L.xn : L.down) <= limit;
+  L.dyn = L.xn_lds && L.xn > L.down ? L.xn : L.down;
+  return L;
+}
+
 struct moe_tail {
   moe_tail_config cfg;
   int device;
   int G;
   size_t lds_dyn;
+  LdsPlan plan;
   unsigned long long deadline_ticks;
   void* scratch;
   mt::Ctl* ctl;
@@ -731,11 +1075,6 @@ static moe_tail_status fail(moe_tail_t* h, moe_tail_status st, const char* fmt, 
   vsnprintf(dst, 256, fmt, ap);
   va_end(ap);
   return st;
-}
-
-static size_t lds_dynamic_bytes(const moe_tail_config* c, int G) {
-  const size_t HR = (size_t)(c->hidden + G - 1) / G;
-  return ((size_t)c->max_rows * c->top_k * HR + (size_t)mt::NW * c->max_rows * HR) * sizeof(float);
 }
 
 extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
@@ -777,9 +1116,10 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
   const int G = prop.multiProcessorCount;
-  const size_t dyn = lds_dynamic_bytes(cfg, G);
   hipFuncAttributes fa;
   HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel));
+  const LdsPlan plan = lds_plan(cfg, G, fa.sharedSizeBytes, (size_t)prop.sharedMemPerBlock);
+  const size_t dyn = plan.dyn;
   if (dyn + fa.sharedSizeBytes > (size_t)prop.sharedMemPerBlock)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", dyn + fa.sharedSizeBytes,
                 (size_t)prop.sharedMemPerBlock);
@@ -795,6 +1135,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->device = dev;
   h->G = G;
   h->lds_dyn = dyn;
+  h->plan = plan;
   const unsigned long long us = cfg->deadline_us ? cfg->deadline_us : 200000u;
   h->deadline_ticks = us * (unsigned long long)wclk_khz / 1000ull;
 
@@ -804,11 +1145,11 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_lg = o_xn + al(R * H * 2);
   const size_t o_as = o_lg + al(R * E * 4), o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
   int prev = 0;
-  hipGetDevice(&prev);
-  hipSetDevice(dev);
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(dev);
   hipError_t e = hipMalloc(&h->scratch, total);
   if (e != hipSuccess) {
-    hipSetDevice(prev);
+    (void)hipSetDevice(prev);
     free(h);
     return fail(nullptr, MOE_TAIL_ENOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
   }
@@ -816,9 +1157,9 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void*)mt::moe_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  hipSetDevice(prev);
+  (void)hipSetDevice(prev);
   if (e != hipSuccess) {
-    hipFree(h->scratch);
+    (void)hipFree(h->scratch);
     free(h);
     return fail(nullptr, MOE_TAIL_EHIP, "scratch setup: %s", hipGetErrorString(e));
   }
@@ -868,7 +1209,16 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.Is = c.shared_inter;
   p.scoring = c.scoring;
   p.G = h->G;
-  p.shp_off = c.max_rows * c.top_k * ((c.hidden + h->G - 1) / h->G);
+  p.xn_lds = h->plan.xn_lds;
+  p.xs = h->plan.xs;
+  p.as = h->plan.as;
+  p.ss = h->plan.ss;
+  p.off_as = h->plan.off_as;
+  p.off_outp = h->plan.off_outp;
+  p.off_shp = h->plan.off_shp;
+  p.xzero = c.max_rows;
+  p.azero = c.max_rows * c.top_k;
+  p.szero = c.max_rows;
   p.eps = (double)c.eps;
   p.deadline_ticks = h->deadline_ticks;
   p.debug_flags = c.debug_flags;
@@ -913,27 +1263,40 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
 
 extern "C" moe_tail_status moe_tail_get_error(moe_tail_t* h) {
   if (!h) return fail(nullptr, MOE_TAIL_EINVAL, "handle is NULL");
-  uint32_t v = 0;
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int prev = 0;
-  hipGetDevice(&prev);
-  hipSetDevice(h->device);
-  hipError_t e = hipMemcpy(&v, &h->ctl->error, 4, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && v) e = hipMemset(&h->ctl->error, 0, 4);
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  hipError_t e = hipMemcpy(w, &h->ctl->error, sizeof(w), hipMemcpyDeviceToHost);
+  const uint32_t v = w[0];
+  if (e == hipSuccess && v) e = hipMemset(&h->ctl->error, 0, sizeof(w));
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  hipSetDevice(prev);
+  (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "reading the error word: %s", hipGetErrorString(e));
-  if (v == MOE_TAIL_ETIMEOUT) return fail(h, MOE_TAIL_ETIMEOUT, "a cross-workgroup wait passed its deadline");
+  static const char* names[4] = {"norm", "router", "shared", "routed"};
+  if (v == MOE_TAIL_ETIMEOUT)
+    return fail(h, MOE_TAIL_ETIMEOUT,
+                "a cross-workgroup wait passed its deadline: %s wait in workgroup %u saw %u of %u (epoch %u, %u slots)",
+                w[1] < 4 ? names[w[1]] : "?", w[2], w[3], w[4], w[5], w[6]);
   return MOE_TAIL_OK;
 }
+
+#ifdef MOE_TAIL_TIMELINE
+// Timeline builds only: copy the last call's stamps ([1024][16] u64) to host.
+extern "C" int moe_tail_debug_timeline(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(mt::g_timeline), sizeof(mt::g_timeline), 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
 
 extern "C" const char* moe_tail_strerror(moe_tail_t* h) { return h ? h->err : g_create_err; }
 
 extern "C" void moe_tail_destroy(moe_tail_t* h) {
   if (!h) return;
   int prev = 0;
-  hipGetDevice(&prev);
-  hipSetDevice(h->device);
-  hipFree(h->scratch);
-  hipSetDevice(prev);
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  (void)hipFree(h->scratch);
+  (void)hipSetDevice(prev);
   free(h);
 }

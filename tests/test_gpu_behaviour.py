@@ -23,12 +23,14 @@ def test_run_to_run_bitwise():
             np.testing.assert_array_equal(a[k], b[k])
 
 
-def test_batch_invariance():
-    """A row's outputs do not depend on the other rows or on the row count."""
+@pytest.mark.parametrize("max_rows", [8, 16])
+def test_batch_invariance(max_rows):
+    """A row's outputs do not depend on the other rows or on the row count.
+    max_rows 8 stages activations in LDS, 16 reads them from global scratch."""
     cfg = synth.CONFIGS["c1"].with_rows(8)
     w = weights("c1")
     x, r, _ = gapped_rows(cfg, w)
-    h = handle_for(cfg, max_rows=16)
+    h = handle_for(cfg, max_rows=max_rows)
     dw = device_weights("c1")
     full = run(h, cfg, dw, x, r)
     for rows in (1, 3, 5):
@@ -62,12 +64,13 @@ def test_exact_ties_go_to_the_lower_expert():
                 assert lo in g["ids"][row]
 
 
-def test_graph_replay_of_mixed_row_counts():
+@pytest.mark.parametrize("max_rows", [8, 16])
+def test_graph_replay_of_mixed_row_counts(max_rows):
     t = pytest.importorskip("torch")
     cfg = synth.CONFIGS["c1"].with_rows(8)
     w = weights("c1")
     x, r, _ = gapped_rows(cfg, w)
-    h = handle_for(cfg, max_rows=16)
+    h = handle_for(cfg, max_rows=max_rows)
     dw = device_weights("c1")
     widths = [8, 1, 3, 8, 2, 5]
     xd, rd = dev(x), dev(r)
