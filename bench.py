@@ -15,6 +15,7 @@ expert, gamma, activations in and out) over the measured time per call.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep/--no-sweep]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,42 @@ from decode_moe_layer_amd import binding, synth  # noqa: E402
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
 METRIC = "µs per MoE-tail call and achieved HBM GB/s (fraction of peak) at 1/8 rows"
 MALL_BYTES = 256 * 2**20
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_tail_kernel_c2_8rows_hbm_traffic.txt")
+KERNEL_SOURCES = (os.path.join(ROOT, "decode_moe_layer_amd", "csrc", "moe_tail.hip"),
+                  os.path.join(ROOT, "include", "moe_tail.h"))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary.
+
+    Each counter's KiB per dispatch is scaled by what the same counter reads for
+    a plain device copy of known size (factors stored in the summary).  Returns
+    None when the summary is absent or was taken on a different kernel source.
+    """
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith((" ", "#", "$")))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    try:
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return int(round((fetch + write) * 1024))
 
 
 def c2_rho():
@@ -267,7 +304,7 @@ def main():
                                "E8M0 block-32), top-10 softmax, I 256, bf16 shared Is 512, ~30% repeated picks",
                    "rows": 8, "distinct_experts": head["distinct_experts"], "weight_copies": head["copies"]},
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": head["frac_of_peak"], "traffic": None,
+                     "frac": head["frac_of_peak"], "traffic": measured_traffic(),
                      "alg_bytes_per_call": head["alg_bytes"]},
         "cpu_baseline": cpu,
         "copy_GBps": round(copy_gbps, 1),

@@ -31,10 +31,11 @@
 // (E2M1 x 2^(s-127) is exact in bf16 for the scales in range), so every
 // product is exact and accumulation is fp32.  A lane's 16-byte weight load is
 // one whole 32-element scale block (PR 85 commit row 18's 16-byte loads);
-// weights are read once per call with nontemporal loads (commit row 21), and
-// each wave keeps a deep window of them in flight, issued ahead of the waits
-// they do not depend on (PR 85: weights are issued before an activation poll
-// is checked).
+// weights are read once per call (the pages use nontemporal loads, commit
+// row 21; here the default policy measured faster, see the buffer-access
+// note below), and each wave keeps a deep window of them in flight, issued
+// ahead of the waits they do not depend on (PR 85: weights are issued before
+// an activation poll is checked).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
