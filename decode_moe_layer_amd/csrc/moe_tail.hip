@@ -69,25 +69,30 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int MAX_U1 = 32 + 512;  // router blocks (E/16) + shared blocks (Is/8)
+constexpr int MAX_G = 1024;        // workgroups (one per compute unit)
+constexpr int NRC = 16;            // routed-arrival counters (workgroup c adds to c % NRC)
+constexpr int MAX_ITEMS1 = 64;     // K-chunk items of the router/shared phase per workgroup
+
+// Arrival counters of one call.  Every counter sits on its own 64-byte line;
+// contention on one address serialises the atomics, so each counter has a
+// small fan-in (at most 16 arrivals, 32 for the router and 512 for the
+// shared blocks, whose waits are off the critical path).
 struct Bank {
-  uint32_t norm;
-  uint32_t _p0[63];
-  uint32_t router;
-  uint32_t _p1[63];
-  uint32_t shared;
-  uint32_t _p2[63];
-  uint32_t routed;
-  uint32_t _p3[63];
-  uint32_t abort_;
-  uint32_t _p4[63];
+  uint32_t normc[NQ][16];     // norm slice q: one arrival per row
+  uint32_t router[16];        // router blocks whose logits are final
+  uint32_t shared[16];        // shared blocks whose activations are final
+  uint32_t routed[NRC][16];   // routed gate/up units done
+  uint32_t abort_[16];        // set by a wait that passed its deadline
+  uint32_t unitc[MAX_U1][16]; // K-chunk partials stored, per router/shared block
 };
+constexpr int BANK_WORDS = (int)(sizeof(Bank) / 4);
 
 struct Ctl {
-  unsigned long long ticket;
-  uint32_t _p0[62];
   uint32_t error;
   uint32_t diag[7];  // first timeout: wait id, workgroup, observed, target, epoch, info
-  uint32_t _p1[56];
+  uint32_t _p0[56];
+  uint32_t cta_ep[MAX_G];  // per workgroup: calls it has started (its epoch)
   Bank bank[2];
 };
 
@@ -95,8 +100,12 @@ struct Params {
   int R, H, E, K, I, Is, scoring, G;
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
   int xs, as, ss;                 // LDS row strides (bf16 elements): xn, routed a, shared a
+  int cs;                         // LDS row stride of the router/shared phase's xn chunk
   int off_as, off_outp, off_shp;  // byte offsets in dynamic LDS (down phase)
   int xzero, azero, szero;        // indices of the all-zero LDS rows (inactive MFMA columns)
+  int n_rb, n_sb;                 // router blocks (16 experts), shared blocks (8 gate + 8 up rows)
+  int S1, TC;                     // K chunks per block, 32-column groups per chunk
+  int Ep;                         // logits row stride (E rounded up to 8)
   double eps;
   unsigned long long deadline_ticks;
   uint32_t debug_flags;
@@ -122,6 +131,7 @@ struct Params {
   Ctl* ctl;
   uint16_t* xn;
   float* logits;
+  float* part1;  // [blocks * S1][16][16] fp32 K-chunk partial sums
   uint16_t* a_s;
   uint16_t* a_r;
 };
@@ -308,35 +318,62 @@ __device__ __forceinline__ void publish(uint32_t* c, uint32_t n) {
   if (threadIdx.x == 0 && n) __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup-uniform wait for *c >= target with a deadline.  Returns false when
-// the launch is aborted (this wait timed out, or another one did).
-__device__ __forceinline__ bool wait_ge(const Params& p, Bank* bk, uint32_t* c, uint32_t target, bool stall,
-                                        uint32_t* s_flag, uint32_t wait_id, uint32_t ep, uint32_t info) {
-  if (threadIdx.x == 0) {
+// Workgroup-uniform wait, polled by wave 0: counters c[k * stride] for k < n
+// (n <= 64) all reach `target` (SUM false) or sum to at least `target` (SUM
+// true).  Every wait has a deadline; a wait that passes it sets the abort
+// word, which ends every other wait of the call.  Returns false when the call
+// is aborted.
+template <bool SUM>
+__device__ __forceinline__ bool wait_cnt(const Params& p, Bank* bk, const uint32_t* c, int stride, int n,
+                                         uint32_t target, bool stall, uint32_t* s_flag, uint32_t wait_id,
+                                         uint32_t ep, uint32_t info) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     uint32_t ok = 1;
     const unsigned long long t0 = wall_clock64();
     while (true) {
-      const uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (v >= target && !stall) break;
-      if (__hip_atomic_load(&bk->abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      const uint32_t v = lane < n ? __hip_atomic_load(c + lane * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : (SUM ? 0u : 0xFFFFFFFFu);
+      uint32_t seen;
+      bool done;
+      if (SUM) {
+        int t = (int)v;
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        seen = (uint32_t)__builtin_amdgcn_readfirstlane(t);
+        done = seen >= target;
+      } else {
+        done = __ballot(v < target) == 0;
+        seen = done ? target : (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+      }
+      if (done && !stall) break;
+      uint32_t ab = 0;
+      if (lane == 0) ab = __hip_atomic_load(&bk->abort_[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane((int)ab)) {
         ok = 0;
         break;
       }
       if (wall_clock64() - t0 > p.deadline_ticks) {
-        __hip_atomic_store(&bk->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t zero = 0;
-        if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          const uint32_t d[6] = {wait_id, blockIdx.x, v, target, ep, info};
-          for (int k = 0; k < 6; ++k)
-            __hip_atomic_store(&p.ctl->diag[k], d[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+          __hip_atomic_store(&bk->abort_[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          uint32_t zero = 0;
+          if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            const uint32_t d[6] = {wait_id, blockIdx.x, seen, target, ep, info};
+            for (int k = 0; k < 6; ++k)
+              __hip_atomic_store(&p.ctl->diag[k], d[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
         ok = 0;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    *s_flag = ok;
+    if (lane == 0) *s_flag = ok;
   }
   __syncthreads();
   const bool ok = *s_flag != 0;
@@ -389,10 +426,11 @@ struct Shared {
   uint32_t ep;
   double tmpd[NW];
   int wcnt[NW];
+  int ucnt[NW];
+  int last[MAX_ITEMS1];
   int16_t ids[MAX_P];
   float w[MAX_P];
   int16_t ci[MAX_P];
-  int minpick[MAX_E];
   uint32_t rowmask[MAX_E];
   int16_t eslot[MAX_E];
   int16_t slot_expert[MAX_P];
@@ -411,35 +449,40 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int R = p.R, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, G = p.G;
   const int P = R * K;
   const int i16 = lane & 15, g = lane >> 4;  // MFMA row / column within 16, K-group
+  const int n_rb = p.n_rb, n_sb = p.n_sb, S1 = p.S1, TC = p.TC;
+  const int n_it = (n_rb + n_sb) * S1;
   const rsrc_t rs_xn = make_rsrc(p.xn, (uint32_t)(R * H * 2));
-  const rsrc_t rs_lg = make_rsrc(p.logits, (uint32_t)(R * E * 4));
+  const rsrc_t rs_lg = make_rsrc(p.logits, (uint32_t)(R * p.Ep * 4));
+  const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * 1024));
   const rsrc_t rs_as = make_rsrc(p.a_s, (uint32_t)(R * Is * 2));
   const rsrc_t rs_ar = make_rsrc(p.a_r, (uint32_t)(P * I * 2));
   uint16_t* xl = (uint16_t*)dyn;  // [xrows][xs] staged activations; row xzero is zeros
+  uint16_t* xc = (uint16_t*)dyn;  // [xrows][cs] this workgroup's K chunk of them (same space, earlier)
   const int xzero = p.xzero;
 
   TL(0);
-  // ---- epoch ticket (its result is needed only at the first exchange)
-  unsigned long long tk = 0;
-  if (tid == 0) tk = __hip_atomic_fetch_add(&p.ctl->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- call epoch: every workgroup counts the calls it has started, so all
+  // agree on it without a shared ticket (one launch = one call per workgroup)
+  uint32_t epv = 0;
+  if (tid == 0) epv = __hip_atomic_load(&p.ctl->cta_ep[cta], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < E) S.rowmask[tid] = 0u;
   const bool stall = (p.debug_flags & MOE_TAIL_DEBUG_STALL) && cta == p.debug_block;
 
-  // ---- P1 source: router row blocks (16 experts) then shared blocks (8 gate + 8 up);
-  // this workgroup's units are cta, cta + G, ...; wave w streams columns [t01, t01 + TP1) of 32
-  const int n_rb = (E + 15) / 16, n_sb = Is / 8, n_p1 = n_rb + n_sb;
-  const int T1 = H / 32, TP1 = (T1 + NW - 1) / NW, t01 = wave * TP1;
-  const int nu1 = cta < n_p1 ? (n_p1 - 1 - cta) / G + 1 : 0;
-  using P1Frag = typename std::conditional<XL, FragA, FragAB>::type;
-  Window<D_BF, P1Frag> w1;
+  // ---- router/shared source.  Item i = cta, cta + G, ... is K chunk i % S1 of
+  // block i / S1 (router blocks of 16 experts, then shared blocks of 8 gate +
+  // 8 up rows); S1 divides G, so all of this workgroup's items share chunk s1.
+  // Wave w streams the chunk's 32-column groups [t01, t1e).
+  const int s1 = cta % S1;
+  const int TP1 = (TC + NW - 1) / NW, t01 = wave * TP1, t1e = min(TC, t01 + TP1);
+  const int nu1 = cta < n_it ? (n_it - 1 - cta) / G + 1 : 0;
+  Window<D_BF, FragA> w1;
   int k1 = 0, t1 = t01;
-  bool r1 = true;
   uint32_t roff1 = OOB;
   rsrc_t rs1 = make_rsrc(p.rw, (uint32_t)((size_t)E * H * 2));
-  auto p1_unit = [&]() {  // decode unit k1
-    const int u = cta + k1 * G;
-    r1 = u < n_rb;
+  auto p1_unit = [&]() {  // decode item k1
+    const int u = (cta + k1 * G) / S1;
     int row;
-    if (r1) {
+    if (u < n_rb) {
       row = u * 16 + i16 < E ? u * 16 + i16 : -1;
       rs1 = make_rsrc(p.rw, (uint32_t)((size_t)E * H * 2));
     } else {
@@ -447,15 +490,13 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       row = i16 < 8 ? sb * 8 + i16 : Is + sb * 8 + (i16 - 8);
       rs1 = make_rsrc(p.ws13, (uint32_t)((size_t)2 * Is * H * 2));
     }
-    roff1 = row >= 0 ? (uint32_t)(row * H + g * 8) * 2u : OOB;
+    roff1 = row >= 0 ? (uint32_t)(row * H + s1 * TC * 32 + g * 8) * 2u : OOB;
   };
   if (nu1) p1_unit();
-  const uint32_t xoff = i16 < R ? (uint32_t)(i16 * H + g * 8) * 2u : OOB;
   auto p1_next = [&]() {
-    P1Frag f;
-    const bool v = k1 < nu1 && t1 < T1;
-    f.a = ld16<CP_W>(rs1, (v && roff1 != OOB) ? roff1 + (uint32_t)t1 * 64u : OOB);
-    if constexpr (!XL) f.b = ld16<CP_SC1>(rs_xn, (v && xoff != OOB) ? xoff + (uint32_t)t1 * 64u : OOB);
+    FragA f;
+    const bool v = k1 < nu1 && t1 < t1e && roff1 != OOB;
+    f.a = ld16<CP_W>(rs1, v ? roff1 + (uint32_t)t1 * 64u : OOB);
     if (++t1 == t01 + TP1) {
       t1 = t01;
       if (++k1 < nu1) p1_unit();
@@ -463,16 +504,16 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     return f;
   };
   const bool is_norm = cta < R * NQ;
-  if constexpr (XL) {
-    if (!is_norm) w1.prime(p1_next);
-  }
+  // weights do not depend on the activations: their loads go out first,
+  // except in the norm workgroups, whose row loads must not queue behind them
+  if (!is_norm) w1.prime(p1_next);
 
-  // ---- P0: fused residual add + RMSNorm; workgroup c < R*NQ owns a slice
+  // ---- P0: fused residual add + RMSNorm; workgroup c < R*NQ owns slice c % NQ of row c / NQ
   if (is_norm) {
-    const int row = cta / NQ, q = cta % NQ;
+    const int row = cta / NQ, q = cta % NQ, SL = H / NQ;
     const rsrc_t rx = make_rsrc(p.x + (size_t)row * H, (uint32_t)(H * 2));
     const rsrc_t rr = make_rsrc(p.res ? p.res + (size_t)row * H : p.x, p.res ? (uint32_t)(H * 2) : 0u);
-    double ss = 0.0;
+    const rsrc_t rg = make_rsrc(p.gamma, (uint32_t)(H * 2));
     u32x4 xv[4], rv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // H <= 16384 = 4 x 512 x 8
@@ -480,6 +521,13 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       xv[k] = ld16<0>(rx, i < H ? (uint32_t)i * 2u : OOB);
       rv[k] = ld16<0>(rr, i < H ? (uint32_t)i * 2u : OOB);
     }
+    // this workgroup's slice, loaded up front as well (8 elements per thread)
+    const int i = q * SL + tid * 8;
+    const bool sl = tid * 8 < SL;
+    const u32x4 x8 = ld16<0>(rx, sl ? (uint32_t)i * 2u : OOB);
+    const u32x4 r8 = ld16<0>(rr, sl ? (uint32_t)i * 2u : OOB);
+    const u32x4 g8 = ld16<0>(rg, sl ? (uint32_t)i * 2u : OOB);
+    double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -496,11 +544,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     double tot = 0.0;
     for (int w = 0; w < NW; ++w) tot += S.tmpd[w];
     const double rstd = 1.0 / sqrt(tot / (double)H + p.eps);
-    const int SL = H / NQ, i = q * SL + tid * 8;
-    if (tid * 8 < SL) {
-      const u32x4 x8 = ld16<0>(rx, (uint32_t)i * 2u);
-      const u32x4 r8 = ld16<0>(rr, (uint32_t)i * 2u);
-      const u32x4 g8 = *(const u32x4*)(p.gamma + i);
+    if (sl) {
       u32x4 hv, nv;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -515,35 +559,132 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
     }
   }
-  if (tid == 0) S.ep = (uint32_t)(tk / (unsigned long long)G);
+  if (tid == 0) {
+    epv += 1;
+    __hip_atomic_store(&p.ctl->cta_ep[cta], epv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S.ep = epv;
+  }
   __syncthreads();
   const uint32_t ep = S.ep;
   Bank* bk = &p.ctl->bank[ep & 1];
-  if (cta == 0) {  // the next call's bank, with write-through (SC1) stores:
-    // a dirty line left in this XCD's L2 could be written back over the
-    // next call's increments
+  if (cta == 0) {  // the next call's counters, with write-through (SC1) stores
     uint32_t* nb = (uint32_t*)&p.ctl->bank[(ep + 1) & 1];
-    for (int i = tid; i < (int)(sizeof(Bank) / 4); i += NT)
+    for (int i = tid * 16; i < BANK_WORDS; i += NT * 16)
       __hip_atomic_store(nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (is_norm) publish(&bk->norm, 1);
-  if constexpr (XL) {
-    if (is_norm) w1.prime(p1_next);
+  if (is_norm) {
+    publish(&bk->normc[cta % NQ][0], 1);
+    w1.prime(p1_next);
   }
   TL(1);
-  if (!wait_ge(p, bk, &bk->norm, (uint32_t)(R * NQ), stall, &S.flags[0], 0, ep, 0)) return;
-  TL(2);
+
+  // ---- router/shared phase: stage this chunk of xn, then the items' MFMA tiles
+  if (nu1) {
+    if (!wait_cnt<false>(p, bk, &bk->normc[s1 * (NQ / S1)][0], 16, NQ / S1, (uint32_t)R, stall, &S.flags[0], 0, ep,
+                         0))
+      return;
+    TL(2);
+    const int CW = TC * 32, c8n = CW / 8, n8 = R * c8n;
+    for (int base = 0; base < n8; base += NT * 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e8 = base + k * NT + tid, r = e8 / c8n, c8 = e8 - r * c8n;
+        v[k] = ld16<CP_SC1>(rs_xn, e8 < n8 ? (uint32_t)(r * H + s1 * CW + c8 * 8) * 2u : OOB);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e8 = base + k * NT + tid, r = e8 / c8n, c8 = e8 - r * c8n;
+        if (e8 < n8) *(u32x4*)(xc + r * p.cs + c8 * 8) = v[k];
+      }
+    }
+    for (int c = tid * 8; c < p.cs; c += NT * 8) *(u32x4*)(xc + xzero * p.cs + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  TL(3);
+  {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int rb = 0, kk = 0, tt = 0;
+    const int brow = (i16 < R ? i16 : xzero) * p.cs + g * 8;  // this lane's activation row in LDS
+    w1.run(nu1 * TP1, p1_next, [&](const FragA& f) {
+      const int t = t01 + tt;
+      const u32x4 b = lds16(xc + (t < t1e ? brow + t * 32 : xzero * p.cs));
+      acc = mfma(as_bf16x8(f.a), as_bf16x8(b), acc);
+      if (++tt == TP1) {  // item done: reduce the 8 waves' partials in wave order, store the chunk's partial
+        tt = 0;
+        const int it = cta + kk * G;
+        ++kk;
+        S.red[rb][wave][lane] = acc;
+        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (tid < 256) {
+          const int l = tid >> 2, qq = tid & 3;
+          float v = 0.f;
+          for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
+          const int row = 4 * (l >> 4) + qq, col = l & 15;
+          if (col < R) stcf(rs_pt, (uint32_t)((it * 16 + row) * 16 + col) * 4u, v);
+        }
+        rb ^= 1;
+      }
+    });
+  }
+  // count this workgroup's chunk arrivals; the last of a block's S1 chunks sums them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid < nu1) {
+    const int u = (cta + tid * G) / S1;
+    const uint32_t old = __hip_atomic_fetch_add(&bk->unitc[u][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S.last[tid] = old == (uint32_t)(S1 - 1);
+  }
+  __syncthreads();
+  {
+    int nr = 0;
+    for (int k = 0; k < nu1; ++k) {  // router blocks: logits = sum of the chunks in chunk order
+      const int u = (cta + k * G) / S1;
+      if (!S.last[k] || u >= n_rb) continue;
+      if (tid < 16 * R) {
+        const int row = tid / R, col = tid - row * R;
+        float v = 0.f;
+        for (int s = 0; s < S1; ++s) v += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
+        const int e = u * 16 + row;
+        if (e < E) stcf(rs_lg, (uint32_t)(col * p.Ep + e) * 4u, v);
+      }
+      ++nr;
+    }
+    if (nr) publish(&bk->router[0], (uint32_t)nr);
+    int ns = 0;
+    for (int k = 0; k < nu1; ++k) {  // shared blocks: a = silu(gate) * up over the summed chunks
+      const int u = (cta + k * G) / S1;
+      if (!S.last[k] || u < n_rb) continue;
+      if (tid < 8 * R) {
+        const int row = tid / R, col = tid - row * R;
+        float gs = 0.f, us = 0.f;
+        for (int s = 0; s < S1; ++s) {
+          gs += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
+          us += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row + 8) * 16 + col) * 4));
+        }
+        const float a = gs / (1.f + __expf(-gs)) * us;
+        stc2(rs_as, (uint32_t)(col * Is + (u - n_rb) * 8 + row) * 2u, f2bf(a));
+      }
+      ++ns;
+    }
+    if (ns) publish(&bk->shared[0], (uint32_t)ns);
+  }
+  TL(4);
+
+  // ---- all of xn, for the routed gate/up phase
+  if (!wait_cnt<false>(p, bk, &bk->normc[0][0], 16, NQ, (uint32_t)R, stall && !nu1, &S.flags[1], 0, ep, 1)) return;
   if constexpr (XL) {  // stage xn [R][H] -> LDS rows of stride xs; row xzero stays zero
     const int n8 = R * H / 8;
-    for (int base = 0; base < n8; base += NT * 4) {
-      u32x4 v[4];
+    for (int base = 0; base < n8; base += NT * 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int e8 = base + k * NT + tid;
         v[k] = ld16<CP_SC1>(rs_xn, e8 < n8 ? (uint32_t)e8 * 16u : OOB);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int e8 = base + k * NT + tid;
         if (e8 < n8) {
           const int r = (e8 * 8) / H, c = (e8 * 8) % H;
@@ -552,186 +693,120 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       }
     }
     for (int c = tid * 8; c < p.xs; c += NT * 8) *(u32x4*)(xl + xzero * p.xs + c) = (u32x4){0u, 0u, 0u, 0u};
-    __syncthreads();
-  } else {
-    w1.prime(p1_next);
   }
-  TL(3);
 
-  // ---- P1: router row blocks and shared gate/up blocks (waves split K)
-  {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int rb = 0, kk = 0, tt = 0;
-    const int brow = (i16 < R ? i16 : xzero) * p.xs + g * 8;  // this lane's activation row in LDS
-    w1.run(nu1 * TP1, p1_next, [&](const P1Frag& f) {
-      const int t = t01 + tt;
-      u32x4 b;
-      if constexpr (XL) {
-        b = lds16(xl + (t < T1 ? brow + t * 32 : xzero * p.xs));
-      } else {
-        b = f.b;
-      }
-      acc = mfma(as_bf16x8(f.a), as_bf16x8(b), acc);
-      if (++tt == TP1) {  // unit done: reduce the 8 waves' partials in wave order
-        tt = 0;
-        const int u = cta + kk * G;
-        ++kk;
-        S.red[rb][wave][lane] = acc;
-        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        __syncthreads();
-        if (u < n_rb) {
-          if (tid < 256) {
-            const int l = tid >> 2, qq = tid & 3;
-            float v = 0.f;
-            for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
-            const int e = u * 16 + 4 * (l >> 4) + qq, col = l & 15;
-            if (e < E && col < R) stcf(rs_lg, (uint32_t)(col * E + e) * 4u, v);
-          }
-        } else {
-          if (tid < 128) {
-            const int l = tid >> 2, qq = tid & 3;
-            float gs = 0.f, us = 0.f;
-            for (int w = 0; w < NW; ++w) {
-              gs += S.red[rb][w][l][qq];
-              us += S.red[rb][w][l + 32][qq];
-            }
-            const int ii = 4 * (l >> 4) + qq, col = l & 15;
-            const float a = gs / (1.f + __expf(-gs)) * us;
-            if (col < R) stc2(rs_as, (uint32_t)(col * Is + (u - n_rb) * 8 + ii) * 2u, f2bf(a));
-          }
-        }
-        rb ^= 1;
-      }
-    });
-    // this workgroup's units are cta, cta + G, ...: the first nr are router blocks
-    const uint32_t nr = cta < n_rb ? (uint32_t)((n_rb - 1 - cta) / G + 1) : 0u;
-    const uint32_t ns = (uint32_t)nu1 - nr;
-    if (nr) publish(&bk->router, nr);
-    if (ns) publish(&bk->shared, ns);
-  }
-  TL(4);
-
-  // ---- top-k on every workgroup (identical inputs, identical result)
-  if (!wait_ge(p, bk, &bk->router, (uint32_t)n_rb, false, &S.flags[1], 1, ep, 0)) return;
+  // ---- top-k on every workgroup (identical inputs, identical result).  Lane l
+  // holds experts 8l..8l+7 as (key, 7 - j) pairs sorted once in descending
+  // order; a round takes the wave-wide largest head, which on equal keys is the
+  // lowest lane and within it the lowest j: the lower expert id ("glm53:
+  // Long-context indexer ...", PR 85 commit row 9: ID order on ties)
+  if (!wait_cnt<false>(p, bk, &bk->router[0], 16, 1, (uint32_t)n_rb, false, &S.flags[2], 1, ep, 0)) return;
   TL(5);
   for (int r = wave; r < R; r += NW) {
-    uint32_t key[8];
-    float lg[8];
+    const int e0 = 8 * lane;
+    const u32x4 la = ld16<CP_SC1>(rs_lg, e0 < E ? (uint32_t)(r * p.Ep + e0) * 4u : OOB);
+    const u32x4 lb = ld16<CP_SC1>(rs_lg, e0 + 4 < E ? (uint32_t)(r * p.Ep + e0 + 4) * 4u : OOB);
+    const float lg[8] = {__uint_as_float(la[0]), __uint_as_float(la[1]), __uint_as_float(la[2]), __uint_as_float(la[3]),
+                         __uint_as_float(lb[0]), __uint_as_float(lb[1]), __uint_as_float(lb[2]), __uint_as_float(lb[3])};
+    uint64_t qv[8];
+    if (p.scoring == MOE_TAIL_SOFTMAX) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int e = lane + 64 * v;
-      const float l = ldcf(rs_lg, e < E ? (uint32_t)(r * E + e) * 4u : OOB);
-      lg[v] = l;
-      const float kf = p.scoring == MOE_TAIL_SOFTMAX ? l : 1.f / (1.f + __expf(-l)) + (e < E ? p.bias[e] : 0.f);
-      key[v] = e < E ? ord_key(kf) : 0u;
-    }
-    uint32_t lmax = key[0];
-    int lslot = 0;
+      for (int j = 0; j < 8; ++j)
+        qv[j] = ((uint64_t)(e0 + j < E ? ord_key(lg[j]) : 0u) << 32) | (uint32_t)(7 - j);
+    } else {
 #pragma unroll
-    for (int v = 1; v < 8; ++v)
-      if (key[v] > lmax) {
-        lmax = key[v];
-        lslot = v;
-      }
-    for (int k = 0; k < K; ++k) {
-      const uint32_t m = wave_max_u32(lmax);
-      const uint64_t bal = __ballot(lmax == m);
-      int id;
-      if (__popcll(bal) == 1) {
-        const int wl = __ffsll((unsigned long long)bal) - 1;
-        id = wl + 64 * __builtin_amdgcn_readlane(lslot, wl);
-      } else {  // exact tie: the lowest expert id among the tied lanes
-        id = wave_min_i32(lmax == m ? lane + 64 * lslot : 0x7FFFFFFF);
-      }
-      float lsel = 0.f;
-      if (lane == (id & 63)) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-          if (v == (id >> 6)) {
-            key[v] = 0u;
-            lsel = lg[v];
-          }
-        lmax = key[0];
-        lslot = 0;
-#pragma unroll
-        for (int v = 1; v < 8; ++v)
-          if (key[v] > lmax) {
-            lmax = key[v];
-            lslot = v;
-          }
-      }
-      lsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsel), id & 63));
-      if (lane == 0) {
-        S.ids[r * K + k] = (int16_t)id;
-        S.w[r * K + k] = lsel;
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + j;
+        const float kf = 1.f / (1.f + __expf(-lg[j])) + (e < E ? p.bias[e] : 0.f);
+        qv[j] = ((uint64_t)(e < E ? ord_key(kf) : 0u) << 32) | (uint32_t)(7 - j);
       }
     }
-    // normalised weights over the K picks (lanes k < K); S.w holds the logits
-    const float l0 = S.w[r * K];
-    float t = 0.f;
-    if (lane < K) {
-      const float l = S.w[r * K + lane];
-      t = p.scoring == MOE_TAIL_SOFTMAX ? __expf(l - l0) : 1.f / (1.f + __expf(-l));
-    }
-    const float sum = wave_sum_f32(t);
-    if (lane < K) S.w[r * K + lane] = t / sum;
+#define MT_CX(a, b)                    \
+  {                                    \
+    const uint64_t x_ = qv[a], y_ = qv[b]; \
+    const bool s_ = y_ > x_;           \
+    qv[a] = s_ ? y_ : x_;              \
+    qv[b] = s_ ? x_ : y_;              \
   }
+    MT_CX(0, 1) MT_CX(2, 3) MT_CX(4, 5) MT_CX(6, 7)
+    MT_CX(0, 2) MT_CX(1, 3) MT_CX(4, 6) MT_CX(5, 7)
+    MT_CX(1, 2) MT_CX(5, 6)
+    MT_CX(0, 4) MT_CX(1, 5) MT_CX(2, 6) MT_CX(3, 7)
+    MT_CX(2, 4) MT_CX(3, 5)
+    MT_CX(1, 2) MT_CX(3, 4) MT_CX(5, 6)
+#undef MT_CX
+    int myid = 0;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t head = (uint32_t)(qv[0] >> 32);
+      const uint32_t m = wave_max_u32(head);
+      const int wl = __ffsll((unsigned long long)__ballot(head == m)) - 1;
+      const int id = 8 * wl + 7 - __builtin_amdgcn_readlane((int)(uint32_t)qv[0], wl);
+      if (lane == wl) {
+#pragma unroll
+        for (int v = 0; v < 7; ++v) qv[v] = qv[v + 1];
+        qv[7] = 0;
+      }
+      if (lane == k) myid = id;
+    }
+    // lane k < K: pick k's logit, read from the lane that holds it
+    float lsel = 0.f;
+    const int src = (myid >> 3) << 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(lg[j])));
+      if ((myid & 7) == j) lsel = v;
+    }
+    const float lmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lsel)));  // pick 0
+    float t = 0.f;
+    if (lane < K) t = p.scoring == MOE_TAIL_SOFTMAX ? __expf(lsel - lmax) : 1.f / (1.f + __expf(-lsel));
+    const float sum = wave_sum_f32(t);
+    if (lane < K) {
+      S.ids[r * K + lane] = (int16_t)myid;
+      S.w[r * K + lane] = t / sum;
+      atomicOr(&S.rowmask[myid], 1u << r);
+    }
+  }
+  __syncthreads();
   TL(6);
 
-  // ---- de-duplication: slot = distinct expert, in order of first pick
-  for (int e = tid; e < E; e += NT) {
-    S.minpick[e] = 0x7FFFFFFF;
-    S.rowmask[e] = 0u;
-  }
-  __syncthreads();
-  if (tid < P) {
-    atomicMin(&S.minpick[S.ids[tid]], tid);
-    atomicOr(&S.rowmask[S.ids[tid]], 1u << (tid / K));
-  }
-  __syncthreads();
+  // ---- de-duplication: one slot per distinct expert, in expert order, with
+  // the rows that picked it; users of slot d are rows [slot_off[d], slot_off[d+1]) of a
   {
-    const bool first = tid < P && S.minpick[S.ids[tid]] == tid;
-    const uint64_t bal = __ballot(first);
-    if (lane == 0) S.wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int base = 0, nslot = 0;
-    for (int w = 0; w < NW; ++w) {
-      base += w < wave ? S.wcnt[w] : 0;
-      nslot += S.wcnt[w];
-    }
-    const int slot = base + __popcll(bal & lanes_below());
-    if (first) {
-      const int e = S.ids[tid];
-      S.eslot[e] = (int16_t)slot;
-      S.slot_expert[slot] = (int16_t)e;
-      S.slot_mask[slot] = (uint16_t)S.rowmask[e];
-    }
-    __syncthreads();
-    // exclusive prefix over slots of the user count m_d (<= 16): bitwise ballots
-    const int m = tid < nslot ? __popc((uint32_t)S.slot_mask[tid]) : 0;
+    const uint32_t m = tid < E ? S.rowmask[tid] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    const int users = __popc(m);  // <= 16
     int pre = 0, tot = 0;
 #pragma unroll
     for (int b = 0; b < 5; ++b) {
-      const uint64_t bb = __ballot((m >> b) & 1);
+      const uint64_t bb = __ballot((users >> b) & 1);
       pre += __popcll(bb & lanes_below()) << b;
       tot += __popcll(bb) << b;
     }
-    if (lane == 0) S.wcnt[wave] = tot;
+    if (lane == 0) {
+      S.wcnt[wave] = __popcll(bal);
+      S.ucnt[wave] = tot;
+    }
     __syncthreads();
-    int off = pre, all = 0;
+    int sb = 0, ub = 0, ns = 0, nus = 0;
     for (int w = 0; w < NW; ++w) {
-      off += w < wave ? S.wcnt[w] : 0;
-      all += S.wcnt[w];
+      const int a = S.wcnt[w], b = S.ucnt[w];
+      if (w < wave) {
+        sb += a;
+        ub += b;
+      }
+      ns += a;
+      nus += b;
     }
-    if (tid < nslot) S.slot_off[tid] = (int16_t)off;
+    if (m) {
+      const int slot = sb + __popcll(bal & lanes_below());
+      S.slot_expert[slot] = (int16_t)tid;
+      S.slot_mask[slot] = (uint16_t)m;
+      S.slot_off[slot] = (int16_t)(ub + pre);
+      S.eslot[tid] = (int16_t)slot;
+    }
     if (tid == 0) {
-      S.slot_off[nslot] = (int16_t)all;
-      S.nslot = nslot;
-    }
-    __syncthreads();
-    if (tid < P) {
-      const int d = S.eslot[S.ids[tid]], r = tid / K;
-      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
+      S.nslot = ns;
+      S.slot_off[ns] = (int16_t)nus;
     }
     __syncthreads();
   }
@@ -742,7 +817,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       if (p.topk_w) p.topk_w[q] = S.w[q];
     }
     if (p.dbg_logits)
-      for (int q = tid; q < R * E; q += NT) p.dbg_logits[q] = ldcf(rs_lg, (uint32_t)q * 4u);
+      for (int q = tid; q < R * E; q += NT) p.dbg_logits[q] = ldcf(rs_lg, (uint32_t)((q / E) * p.Ep + q % E) * 4u);
   }
   TL(7);
 
@@ -750,7 +825,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   {
     const int UB = I / 8, n_p2 = D * UB;
     const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW, t02 = wave * TP2;
-    const int u0 = (cta - n_p1 % G + G) % G;
+    const int u0 = cta;
     const int nu2 = u0 < n_p2 ? (n_p2 - 1 - u0) / G + 1 : 0;
     const size_t S13 = (size_t)2 * I * (H / 2), S13s = (size_t)2 * I * (H / 32);
     using P2Frag = typename std::conditional<XL, FragQ, FragQB>::type;
@@ -837,7 +912,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         if (++kk < nu2) p2_user();
       }
     });
-    if (nu2) publish(&bk->routed, (uint32_t)nu2);
+    if (nu2) publish(&bk->routed[cta % NRC][0], (uint32_t)nu2);
   }
   TL(8);
 
@@ -882,11 +957,17 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   Window<D_DOWN, FragDown> w3;
   w3.prime(p3_next);
   TL(9);
-  if (Is > 0 && !wait_ge(p, bk, &bk->shared, (uint32_t)n_sb, false, &S.flags[2], 2, ep, (uint32_t)D)) return;
-  if (!wait_ge(p, bk, &bk->routed, (uint32_t)(D * (I / 8)), false, &S.flags[3], 3, ep, (uint32_t)D)) return;
+  if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
+    return;
+  if (!wait_cnt<true>(p, bk, &bk->routed[0][0], 16, NRC, (uint32_t)(D * (I / 8)), false, &S.flags[4], 3, ep, (uint32_t)D))
+    return;
   if (hn == 0) return;
   TL(10);
   {  // stage the routed a [P][I] and the shared a [R][Is] into LDS, plus their zero rows
+    if (tid < P) {  // pick -> its product row: the slot's users in row order
+      const int d = S.eslot[S.ids[tid]], r = tid / K;
+      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
+    }
     const int nr8 = P * I / 8, ns8 = R * Is / 8, n8 = nr8 + ns8;
     for (int base = 0; base < n8; base += NT * 4) {
       u32x4 v[4];
@@ -1024,21 +1105,23 @@ __global__ __launch_bounds__(NT, 1) void moe_tail_kernel(Params p) {
 
 // ==================================================================== host ==
 
-// Dynamic LDS plan.  The gate/up phases stage xn [rows][H + pad] when it
-// fits; the down phase (which reuses the same space) stages the routed a
-// [picks][I + pad], the shared a [rows][Is + pad], the per-pick products
-// [picks][HR] and the shared partials [waves][rows][HR].
+// Dynamic LDS plan.  The router/shared phase stages its K chunk of xn
+// [rows][H/S1 + pad]; the routed gate/up phase then stages all of xn
+// [rows][H + pad] when it fits; the down phase (which reuses the same space)
+// stages the routed a [picks][I + pad], the shared a [rows][Is + pad], the
+// per-pick products [picks][HR] and the shared partials [waves][rows][HR].
 struct LdsPlan {
-  int xn_lds, xs, as, ss, off_as, off_outp, off_shp;
-  size_t down, xn, dyn;
+  int xn_lds, xs, cs, as, ss, off_as, off_outp, off_shp;
+  size_t down, xn, chunk, dyn;
 };
 
 static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
-static LdsPlan lds_plan(const moe_tail_config* c, int G, size_t static_bytes, size_t limit) {
+static LdsPlan lds_plan(const moe_tail_config* c, int G, int TC, size_t static_bytes, size_t limit) {
   LdsPlan L;
   const size_t R = c->max_rows, P = (size_t)c->max_rows * c->top_k, HR = (size_t)(c->hidden + G - 1) / G;
   L.xs = c->hidden + mt::XPAD;
+  L.cs = TC * 32 + mt::XPAD;
   L.as = c->inter + mt::XPAD;
   L.ss = c->shared_inter + mt::XPAD;
   L.off_as = (int)al16((P + 1) * L.as * 2);
@@ -1046,9 +1129,20 @@ static LdsPlan lds_plan(const moe_tail_config* c, int G, size_t static_bytes, si
   L.off_shp = (int)(L.off_outp + al16(P * HR * 4));
   L.down = L.off_shp + al16((size_t)mt::NW * R * HR * 4);
   L.xn = (R + 1) * (size_t)L.xs * 2;
-  L.xn_lds = static_bytes + (L.xn > L.down ? L.xn : L.down) <= limit;
-  L.dyn = L.xn_lds && L.xn > L.down ? L.xn : L.down;
+  L.chunk = (R + 1) * (size_t)L.cs * 2;
+  const size_t base = L.down > L.chunk ? L.down : L.chunk;
+  L.xn_lds = static_bytes + (L.xn > base ? L.xn : base) <= limit;
+  L.dyn = L.xn_lds && L.xn > base ? L.xn : base;
   return L;
+}
+
+// K chunks per router/shared block: the smallest power of two (<= 16, dividing
+// the workgroup count and H/32) that gives every workgroup a router chunk.
+static int chunks_per_block(int H, int E, int G) {
+  const int T1 = H / 32, n_rb = (E + 15) / 16;
+  int S1 = 1;
+  while (S1 < mt::NQ && n_rb * S1 < G && T1 % (2 * S1) == 0 && G % (2 * S1) == 0) S1 *= 2;
+  return S1;
 }
 
 struct moe_tail {
@@ -1062,8 +1156,10 @@ struct moe_tail {
   mt::Ctl* ctl;
   uint16_t* xn;
   float* logits;
+  float* part1;
   uint16_t* a_s;
   uint16_t* a_r;
+  int S1, TC, n_rb, n_sb, Ep;
   char err[256];
 };
 
@@ -1119,7 +1215,13 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   const int G = prop.multiProcessorCount;
   hipFuncAttributes fa;
   HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel));
-  const LdsPlan plan = lds_plan(cfg, G, fa.sharedSizeBytes, (size_t)prop.sharedMemPerBlock);
+  if (G > mt::MAX_G) return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d compute units, at most %d supported", G, mt::MAX_G);
+  const int S1 = chunks_per_block(cfg->hidden, cfg->num_experts, G), TC = cfg->hidden / 32 / S1;
+  const int n_rb = (cfg->num_experts + 15) / 16, n_sb = cfg->shared_inter / 8;
+  const int n_it = (n_rb + n_sb) * S1;
+  if ((n_it + G - 1) / G > mt::MAX_ITEMS1)
+    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d router/shared items exceed %d per workgroup", n_it, mt::MAX_ITEMS1);
+  const LdsPlan plan = lds_plan(cfg, G, TC, fa.sharedSizeBytes, (size_t)prop.sharedMemPerBlock);
   const size_t dyn = plan.dyn;
   if (dyn + fa.sharedSizeBytes > (size_t)prop.sharedMemPerBlock)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", dyn + fa.sharedSizeBytes,
@@ -1139,12 +1241,19 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->plan = plan;
   const unsigned long long us = cfg->deadline_us ? cfg->deadline_us : 200000u;
   h->deadline_ticks = us * (unsigned long long)wclk_khz / 1000ull;
+  h->S1 = S1;
+  h->TC = TC;
+  h->n_rb = n_rb;
+  h->n_sb = n_sb;
+  h->Ep = (cfg->num_experts + 7) & ~7;
 
   const size_t R = cfg->max_rows, H = cfg->hidden, E = cfg->num_experts, K = cfg->top_k;
   const size_t I = cfg->inter, Is = cfg->shared_inter;
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_lg = o_xn + al(R * H * 2);
-  const size_t o_as = o_lg + al(R * E * 4), o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
+  const size_t o_pt = o_lg + al(R * (size_t)h->Ep * 4), o_as = o_pt + al((size_t)n_it * 1024);
+  const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
+  (void)E;
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(dev);
@@ -1168,6 +1277,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->ctl = (mt::Ctl*)(base + o_ctl);
   h->xn = (uint16_t*)(base + o_xn);
   h->logits = (float*)(base + o_lg);
+  h->part1 = (float*)(base + o_pt);
   h->a_s = (uint16_t*)(base + o_as);
   h->a_r = (uint16_t*)(base + o_ar);
   snprintf(h->err, sizeof(h->err), "no error");
@@ -1212,6 +1322,12 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
   p.xs = h->plan.xs;
+  p.cs = h->plan.cs;
+  p.n_rb = h->n_rb;
+  p.n_sb = h->n_sb;
+  p.S1 = h->S1;
+  p.TC = h->TC;
+  p.Ep = h->Ep;
   p.as = h->plan.as;
   p.ss = h->plan.ss;
   p.off_as = h->plan.off_as;
@@ -1245,6 +1361,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.ctl = h->ctl;
   p.xn = h->xn;
   p.logits = h->logits;
+  p.part1 = h->part1;
   p.a_s = h->a_s;
   p.a_r = h->a_r;
 
