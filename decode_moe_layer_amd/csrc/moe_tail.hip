@@ -59,9 +59,7 @@ constexpr int MAX_K = 32;
 constexpr int MAX_P = MAX_R * MAX_K;  // picks per call
 constexpr int MAX_BLK = 2;            // 16-row down blocks per workgroup
 constexpr int D_BF = 12;              // bf16 weight loads in flight per wave
-constexpr int D_FP4 = 12;             // MXFP4 weight loads in flight per wave
-constexpr int D_FP4_G = 4;            // ... when activations come from global memory
-constexpr int D_DOWN = 8;             // down-projection items in flight per wave
+constexpr int D_FP4_G = 4;            // MXFP4 items in flight per wave when activations come from global memory
 constexpr int XPAD = 8;               // bf16 padding per LDS activation row
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -408,14 +406,18 @@ struct FragQ {  // MXFP4: codes + the 4 block scales of this instruction's chunk
   u32x4 a;
   uint32_t s;
 };
+struct FragU {  // MXFP4: up to 8 column groups of one unit, with their block-scale dwords
+  u32x4 a[8];
+  u32x4 s[2];
+};
 struct FragQB {
   u32x4 a;
   uint32_t s;
   u32x4 b[4];
 };
-struct FragDown {
-  u32x4 a[MAX_BLK];
-  uint32_t s[MAX_BLK];
+struct FragD {  // MXFP4 down: up to 4 column groups x both row blocks, with their block scales
+  u32x4 a[4][MAX_BLK];
+  u32x4 s[MAX_BLK];
 };
 struct FragSD {
   u32x4 a[MAX_BLK];
@@ -828,90 +830,133 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     const int u0 = cta;
     const int nu2 = u0 < n_p2 ? (n_p2 - 1 - u0) / G + 1 : 0;
     const size_t S13 = (size_t)2 * I * (H / 2), S13s = (size_t)2 * I * (H / 32);
-    using P2Frag = typename std::conditional<XL, FragQ, FragQB>::type;
-    // source cursor: unit k2, column group t2
-    int k2 = 0, t2 = t02;
-    rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
-    uint32_t qoff = 0, soff = 0, boff = OOB;
-    auto p2_unit = [&]() {
-      const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
-      const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
-      rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
-      rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
-      const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
-      qoff = (uint32_t)(wrow * (H / 2) + g * 16);
-      soff = (uint32_t)(wrow * (H / 32));
-      if constexpr (!XL) {
+    int rb = 0;
+    // end of unit u: reduce the 8 waves' partials in wave order; a = silu(gate) * up
+    auto p2_reduce = [&](f32x4 acc, int u) {
+      const int d = u / UB, bb = u - d * UB;
+      const int m = __popc((uint32_t)S.slot_mask[d]);
+      S.red[rb][wave][lane] = acc;
+      __syncthreads();
+      if (tid < 128) {
+        const int l = tid >> 2, qq = tid & 3;
+        float gs = 0.f, us = 0.f;
+        for (int w = 0; w < NW; ++w) {
+          gs += S.red[rb][w][l][qq];
+          us += S.red[rb][w][l + 32][qq];
+        }
+        const int ii = 4 * (l >> 4) + qq, col = l & 15;
+        const float a = gs / (1.f + __expf(-gs)) * us;
+        if (col < m) stc2(rs_ar, (uint32_t)((S.slot_off[d] + col) * I + bb * 8 + ii) * 2u, f2bf(a));
+      }
+      rb ^= 1;
+    };
+    if constexpr (XL) {
+      // A frag is one part (up to 8 column groups) of a unit: its code loads and
+      // the block-scale dwords of those column groups (lane (i16, g) loads dwords
+      // tb .. tb+7 of its row; column group tb + tt uses dword tt, byte g), so a
+      // unit costs one or two scale loads instead of one per column group.
+      const int NP = (TP2 + 7) / 8;
+      int k2 = 0, q2 = 0;
+      auto p2_next = [&]() {
+        FragU f;
+        const bool v = k2 < nu2;
+        const int u = u0 + (v ? k2 : 0) * G, d = u / UB, b = u - d * UB;
+        const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
+        const rsrc_t rq = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
+        const rsrc_t rs = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
+        const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
+        const int tb = t02 + 8 * q2, np = min(8, TP2 - 8 * q2);
+        const uint32_t qoff = (uint32_t)(wrow * (H / 2) + g * 16), soff = (uint32_t)(wrow * (H / 32) + tb * 4);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (t < np) f.a[t] = ld16<CP_W>(rq, (v && tb + t < T2) ? qoff + (uint32_t)(tb + t) * 64u : OOB);
+        f.s[0] = ld16<CP_W>(rs, v ? soff : OOB);
+        if (np > 4) f.s[1] = ld16<CP_W>(rs, v ? soff + 16u : OOB);
+        if (++q2 == NP) {
+          q2 = 0;
+          ++k2;
+        }
+        return f;
+      };
+      Window<2, FragU> w2;
+      w2.prime(p2_next);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int kk = 0, qc = 0;
+      if (nu2 && TL_ON) TL(13);
+      w2.run(nu2 * NP, p2_next, [&](const FragU& f) {
+        const int u = u0 + kk * G, d = u / UB;
+        const uint32_t mask = S.slot_mask[d];
+        const int brow = (i16 < __popc(mask) ? nth_bit(mask, i16) : xzero) * p.xs + g * 32;
+        const int tb = t02 + 8 * qc, np = min(8, TP2 - 8 * qc);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          if (tt < np) {
+            const int t = tb + tt;
+            const float sc = e8m0f((f.s[tt >> 2][tt & 3] >> (8 * g)) & 0xFFu);
+            u32x4 bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bq[q] = lds16(xl + (t < T2 ? brow + t * 128 + 8 * q : xzero * p.xs));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[tt][q], sc), as_bf16x8(bq[q]), acc);
+          }
+        }
+        if (++qc == NP) {
+          qc = 0;
+          p2_reduce(acc, u);
+          acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+          if (kk < 12) TL(14 + kk);
+          ++kk;
+        }
+      });
+    } else {
+      // activations from global memory: one column group per frag, with its B fragments
+      int k2 = 0, t2 = t02;
+      rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
+      uint32_t qoff = 0, soff = 0, boff = OOB;
+      auto p2_unit = [&]() {
+        const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
+        const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
+        rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
+        rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
+        const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
+        qoff = (uint32_t)(wrow * (H / 2) + g * 16);
+        soff = (uint32_t)(wrow * (H / 32));
         const uint32_t mask = S.slot_mask[d];
         boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
-      }
-    };
-    if (nu2) p2_unit();
-    auto p2_next = [&]() {
-      P2Frag f;
-      const bool v = k2 < nu2 && t2 < T2;
-      f.a = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * 64u : OOB);
-      f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
-      if constexpr (!XL) {
+      };
+      if (nu2) p2_unit();
+      auto p2_next = [&]() {
+        FragQB f;
+        const bool v = k2 < nu2 && t2 < T2;
+        f.a = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * 64u : OOB);
+        f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           f.b[q] = ld16<CP_SC1>(rs_xn, (v && boff != OOB) ? boff + (uint32_t)(t2 * 256 + 16 * q) : OOB);
-      }
-      if (++t2 == t02 + TP2) {
-        t2 = t02;
-        if (++k2 < nu2) p2_unit();
-      }
-      return f;
-    };
-    Window<XL ? D_FP4 : D_FP4_G, P2Frag> w2;
-    w2.prime(p2_next);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int rb = 0, kk = 0, tt = 0, brow = 0, d = 0, m = 0;
-    auto p2_user = [&]() {  // consumer side of unit kk
-      const int u = u0 + kk * G;
-      d = u / UB;
-      const uint32_t mask = S.slot_mask[d];
-      m = __popc(mask);
-      brow = (i16 < m ? nth_bit(mask, i16) : xzero) * p.xs + g * 32;
-    };
-    if (nu2) p2_user();
-    if (nu2 && TL_ON) TL(13);
-    w2.run(nu2 * TP2, p2_next, [&](const P2Frag& f) {
-      const int t = t02 + tt;
-      const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
-      u32x4 b[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (XL) {
-          b[q] = lds16(xl + (t < T2 ? brow + t * 128 + 8 * q : xzero * p.xs));
-        } else {
-          b[q] = f.b[q];
+        if (++t2 == t02 + TP2) {
+          t2 = t02;
+          if (++k2 < nu2) p2_unit();
         }
-      }
+        return f;
+      };
+      Window<D_FP4_G, FragQB> w2;
+      w2.prime(p2_next);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int kk = 0, tt = 0;
+      if (nu2 && TL_ON) TL(13);
+      w2.run(nu2 * TP2, p2_next, [&](const FragQB& f) {
+        const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[q], sc), as_bf16x8(b[q]), acc);
-      if (++tt == TP2) {
-        tt = 0;
-        const int u = u0 + kk * G, bb = u - d * UB;
-        S.red[rb][wave][lane] = acc;
-        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        __syncthreads();
-        if (tid < 128) {
-          const int l = tid >> 2, qq = tid & 3;
-          float gs = 0.f, us = 0.f;
-          for (int w = 0; w < NW; ++w) {
-            gs += S.red[rb][w][l][qq];
-            us += S.red[rb][w][l + 32][qq];
-          }
-          const int ii = 4 * (l >> 4) + qq, col = l & 15;
-          const float a = gs / (1.f + __expf(-gs)) * us;
-          if (col < m) stc2(rs_ar, (uint32_t)((S.slot_off[d] + col) * I + bb * 8 + ii) * 2u, f2bf(a));
+        for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[q], sc), as_bf16x8(f.b[q]), acc);
+        if (++tt == TP2) {
+          tt = 0;
+          p2_reduce(acc, u0 + kk * G);
+          acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+          if (kk < 12) TL(14 + kk);
+          ++kk;
         }
-        if (kk < 12) TL(14 + kk);
-        rb ^= 1;
-        if (++kk < nu2) p2_user();
-      }
-    });
+      });
+    }
     if (nu2) publish(&bk->routed[cta % NRC][0], (uint32_t)nu2);
   }
   TL(8);
@@ -928,33 +973,53 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   float* s_outp = (float*)(dyn + p.off_outp);   // [P][HR]
   float* s_shp = (float*)(dyn + p.off_shp);     // [NW][R][HR]
   const int azero = p.azero, szero = p.szero;
-  // source cursor: slot j3 (slot d = wave + NW * j3), column group t3
-  int j3 = 0, t3 = 0;
-  rsrc_t rq3 = rs_xn, rsc3 = rs_xn;
-  auto p3_slot = [&]() {
-    const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]);  // uniform: scalar descriptors
-    rq3 = make_rsrc(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
-    rsc3 = make_rsrc(p.w2s + e * S2s + (size_t)h0 * CI, (uint32_t)(hn * CI));
-  };
-  if (nsl && hn) p3_slot();
+  // source: frags of up to 4 column groups (of 128 I-elements) of slot j3 (slot
+  // d = wave + NW * j3), both 16-row blocks, with their block scales: when the
+  // scale rows are whole dwords, one 16-byte load per block gives lane (i16, g)
+  // dwords 4 q3 .. 4 q3 + 3 of its row (column group 4 q3 + t uses dword t, byte
+  // g); otherwise one byte per column group.
+  const int NP3 = (TI + 3) / 4;
+  const bool s4 = (CI & 3) == 0;
+  int j3 = 0, q3 = 0;
   auto p3_next = [&]() {
-    FragDown f;
-    const int c = 4 * t3 + g;
-    const bool v = j3 < nsl && hn > 0 && c < CI;
+    FragD f;
+    const bool v = j3 < nsl && hn > 0;
+    const int e = v ? __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]) : 0;  // uniform
+    const rsrc_t rq = make_rsrc(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
+    const rsrc_t rs = make_rsrc(p.w2s + e * S2s + (size_t)h0 * CI, (uint32_t)(hn * CI));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int t3 = 4 * q3 + t, c = 4 * t3 + g;
+      if (t3 < TI) {
+#pragma unroll
+        for (int bl = 0; bl < MAX_BLK; ++bl) {
+          const int hh = 16 * bl + i16;
+          if (bl < nblk) f.a[t][bl] = ld16<CP_W>(rq, (v && hh < hn && c < CI) ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
+        }
+      }
+    }
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) {
       const int hh = 16 * bl + i16;
-      const bool vv = v && bl < nblk && hh < hn;
-      f.a[bl] = ld16<CP_W>(rq3, vv ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
-      f.s[bl] = ld1<CP_W>(rsc3, vv ? (uint32_t)(hh * CI + c) : OOB);
+      if (bl < nblk) {
+        if (s4) {
+          f.s[bl] = ld16<CP_W>(rs, (v && hh < hn) ? (uint32_t)(hh * CI + 16 * q3) : OOB);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int t3 = 4 * q3 + t, c = 4 * t3 + g;
+            f.s[bl][t] = ld1<CP_W>(rs, (v && hh < hn && c < CI) ? (uint32_t)(hh * CI + c) : OOB);
+          }
+        }
+      }
     }
-    if (++t3 == TI) {
-      t3 = 0;
-      if (++j3 < nsl && hn) p3_slot();
+    if (++q3 == NP3) {
+      q3 = 0;
+      ++j3;
     }
     return f;
   };
-  Window<D_DOWN, FragDown> w3;
+  Window<2, FragD> w3;
   w3.prime(p3_next);
   TL(9);
   if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
@@ -1031,34 +1096,36 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       }
     }
   }
-  // routed down: slot d on wave d % NW; items (slot, t) with t over I/128
+  // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
   {
     f32x4 acc[MAX_BLK];
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    int ju = 0, tu = 0, m = 0, ci0 = 0, arow = 0;
-    auto p3_user = [&]() {
+    int ju = 0, qu = 0;
+    w3.run(nsl * NP3, p3_next, [&](const FragD& f) {
       const int d = wave + NW * ju;
-      m = __popc((uint32_t)S.slot_mask[d]);
-      ci0 = S.slot_off[d];
-      arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
-    };
-    if (nsl) p3_user();
-    w3.run(nsl * TI, p3_next, [&](const FragDown& f) {
-      const int c = 4 * tu + g;
-      u32x4 b[4];
+      const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
+      const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + tu * 128 + 8 * q : azero * p.as));
+      for (int t = 0; t < 4; ++t) {
+        const int t3 = 4 * qu + t, c = 4 * t3 + g;
+        if (t3 < TI) {
+          u32x4 b[4];
 #pragma unroll
-      for (int bl = 0; bl < MAX_BLK; ++bl) {
-        if (bl < nblk) {
-          const float sc = e8m0f(f.s[bl] & 0xFFu);
+          for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + t3 * 128 + 8 * q : azero * p.as));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[bl][q], sc), as_bf16x8(b[q]), acc[bl]);
+          for (int bl = 0; bl < MAX_BLK; ++bl) {
+            if (bl < nblk) {
+              const uint32_t sb = s4 ? (f.s[bl][t] >> (8 * g)) : f.s[bl][t];
+              const float sc = e8m0f(sb & 0xFFu);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[t][bl][q], sc), as_bf16x8(b[q]), acc[bl]);
+            }
+          }
         }
       }
-      if (++tu == TI) {
-        tu = 0;
+      if (++qu == NP3) {
+        qu = 0;
 #pragma unroll
         for (int bl = 0; bl < MAX_BLK; ++bl) {
           if (bl < nblk) {
@@ -1070,7 +1137,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           }
           acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        if (++ju < nsl) p3_user();
+        ++ju;
       }
     });
   }
