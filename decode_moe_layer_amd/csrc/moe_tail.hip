@@ -439,6 +439,8 @@ struct Shared {
   uint16_t slot_mask[MAX_P];
   int16_t slot_off[MAX_P + 1];
   int nslot;
+  int nls;
+  int16_t lsb[MAX_ITEMS1];  // shared blocks this workgroup finishes
   f32x4 red[2][NW][64];
 };
 
@@ -654,21 +656,28 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       ++nr;
     }
     if (nr) publish(&bk->router[0], (uint32_t)nr);
-    int ns = 0;
-    for (int k = 0; k < nu1; ++k) {  // shared blocks: a = silu(gate) * up over the summed chunks
-      const int u = (cta + k * G) / S1;
-      if (!S.last[k] || u < n_rb) continue;
-      if (tid < 8 * R) {
-        const int row = tid / R, col = tid - row * R;
-        float gs = 0.f, us = 0.f;
-        for (int s = 0; s < S1; ++s) {
-          gs += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
-          us += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row + 8) * 16 + col) * 4));
-        }
-        const float a = gs / (1.f + __expf(-gs)) * us;
-        stc2(rs_as, (uint32_t)(col * Is + (u - n_rb) * 8 + row) * 2u, f2bf(a));
+    // shared blocks: a = silu(gate) * up over the chunks summed in chunk order,
+    // all of this workgroup's blocks at once (one round trip for the partials)
+    if (tid == 0) {
+      int ns = 0;
+      for (int k = 0; k < nu1; ++k) {
+        const int u = (cta + k * G) / S1;
+        if (S.last[k] && u >= n_rb) S.lsb[ns++] = (int16_t)(u - n_rb);
       }
-      ++ns;
+      S.nls = ns;
+    }
+    __syncthreads();
+    const int ns = S.nls;
+    for (int idx = tid; idx < ns * 8 * R; idx += NT) {
+      const int k = idx / (8 * R), rc = idx - k * 8 * R, row = rc / R, col = rc - row * R;
+      const int sb = S.lsb[k], u = n_rb + sb;
+      float gs = 0.f, us = 0.f;
+      for (int s = 0; s < S1; ++s) {
+        gs += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
+        us += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row + 8) * 16 + col) * 4));
+      }
+      const float a = gs / (1.f + __expf(-gs)) * us;
+      stc2(rs_as, (uint32_t)(col * Is + sb * 8 + row) * 2u, f2bf(a));
     }
     if (ns) publish(&bk->shared[0], (uint32_t)ns);
   }
