@@ -38,6 +38,7 @@
 // an activation poll is checked).
 
 #include <hip/hip_runtime.h>
+#include <vector>
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -90,13 +91,14 @@ struct Ctl {
   uint32_t error;
   uint32_t diag[7];  // first timeout: wait id, workgroup, observed, target, epoch, info
   uint32_t _p0[56];
-  uint32_t cta_ep[MAX_G];  // per workgroup: calls it has started (its epoch)
+  uint32_t cta_ep[MAX_G][16];  // per workgroup, one line each: calls it has started (its epoch)
   Bank bank[2];
 };
 
 struct Params {
   int R, H, E, K, I, Is, scoring, G;
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
+  int rsum;                       // top-k readers sum the router K-chunk partials themselves
   int xs, as, ss;                 // LDS row strides (bf16 elements): xn, routed a, shared a
   int cs;                         // LDS row stride of the router/shared phase's xn chunk
   int off_as, off_outp, off_shp;  // byte offsets in dynamic LDS (down phase)
@@ -349,15 +351,19 @@ __device__ __forceinline__ bool wait_cnt(const Params& p, Bank* bk, const uint32
         seen = done ? target : (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
       }
       if (done && !stall) break;
+      // this call's abort word, and the sticky error of an earlier call that
+      // has not been read yet: a handle in error fails fast instead of
+      // waiting out one deadline per call
       uint32_t ab = 0;
       if (lane == 0) ab = __hip_atomic_load(&bk->abort_[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_readfirstlane((int)ab)) {
+      if (lane == 1) ab = __hip_atomic_load(&p.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__ballot(ab != 0u)) {
         ok = 0;
         break;
       }
       if (wall_clock64() - t0 > p.deadline_ticks) {
         if (lane == 0) {
-          __hip_atomic_store(&bk->abort_[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(&bk->abort_[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           uint32_t zero = 0;
           if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -443,10 +449,11 @@ struct Shared {
   int16_t lsb[MAX_ITEMS1];  // shared blocks this workgroup finishes
   f32x4 red[2][NW][64];
 };
+constexpr int RED_FLOATS = 2 * NW * 64 * 4;  // floats in Shared::red
 
 // ------------------------------------------------------------------ kernel --
 
-template <bool XL>
+template <bool XL, bool RS>
 __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int tid = threadIdx.x, lane = tid & 63, cta = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -466,9 +473,16 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 
   TL(0);
   // ---- call epoch: every workgroup counts the calls it has started, so all
-  // agree on it without a shared ticket (one launch = one call per workgroup)
+  // agree on it without a shared ticket (one launch = one call per workgroup).
+  // The count is a read-modify-write atomic, like every other control word
+  // that crosses workgroups or calls; nothing waits for its return until the
+  // epoch is first needed.
   uint32_t epv = 0;
-  if (tid == 0) epv = __hip_atomic_load(&p.ctl->cta_ep[cta], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    int z;  // an index the compiler cannot see is uniform: the atomic is issued as written, with no wait after it
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    epv = __hip_atomic_fetch_add(&p.ctl->cta_ep[cta][z], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (tid < E) S.rowmask[tid] = 0u;
   const bool stall = (p.debug_flags & MOE_TAIL_DEBUG_STALL) && cta == p.debug_block;
 
@@ -564,9 +578,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
   }
   if (tid == 0) {
-    epv += 1;
-    __hip_atomic_store(&p.ctl->cta_ep[cta], epv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    S.ep = epv;
+    uint32_t e1 = epv;
+    asm volatile("" : "+v"(e1));  // keeps the wait for the atomic's return here
+    S.ep = e1 + 1u;
   }
   __syncthreads();
   const uint32_t ep = S.ep;
@@ -574,7 +588,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   if (cta == 0) {  // the next call's counters, with write-through (SC1) stores
     uint32_t* nb = (uint32_t*)&p.ctl->bank[(ep + 1) & 1];
     for (int i = tid * 16; i < BANK_WORDS; i += NT * 16)
-      __hip_atomic_store(nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      (void)__hip_atomic_exchange(nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (is_norm) {
     publish(&bk->normc[cta % NQ][0], 1);
@@ -626,7 +640,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           float v = 0.f;
           for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
           const int row = 4 * (l >> 4) + qq, col = l & 15;
-          if (col < R) stcf(rs_pt, (uint32_t)((it * 16 + row) * 16 + col) * 4u, v);
+          if (col < R) stcf(rs_pt, (uint32_t)((it * 16 + col) * 16 + row) * 4u, v);
         }
         rb ^= 1;
       }
@@ -645,11 +659,17 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     int nr = 0;
     for (int k = 0; k < nu1; ++k) {  // router blocks: logits = sum of the chunks in chunk order
       const int u = (cta + k * G) / S1;
-      if (!S.last[k] || u >= n_rb) continue;
+      if (!S.last[k] || u >= n_rb || RS) continue;
       if (tid < 16 * R) {
-        const int row = tid / R, col = tid - row * R;
+        const int col = tid >> 4, row = tid & 15;
+        float t[NQ];
+#pragma unroll
+        for (int s = 0; s < NQ; ++s)
+          if (s < S1) t[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row) * 4));
         float v = 0.f;
-        for (int s = 0; s < S1; ++s) v += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
+#pragma unroll
+        for (int s = 0; s < NQ; ++s)
+          if (s < S1) v += t[s];
         const int e = u * 16 + row;
         if (e < E) stcf(rs_lg, (uint32_t)(col * p.Ep + e) * 4u, v);
       }
@@ -669,13 +689,22 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     __syncthreads();
     const int ns = S.nls;
     for (int idx = tid; idx < ns * 8 * R; idx += NT) {
-      const int k = idx / (8 * R), rc = idx - k * 8 * R, row = rc / R, col = rc - row * R;
+      const int k = idx / (8 * R), rc = idx - k * 8 * R, col = rc >> 3, row = rc & 7;
       const int sb = S.lsb[k], u = n_rb + sb;
+      float tg[NQ], tu[NQ];
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1) {
+          tg[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row) * 4));
+          tu[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row + 8) * 4));
+        }
       float gs = 0.f, us = 0.f;
-      for (int s = 0; s < S1; ++s) {
-        gs += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row) * 16 + col) * 4));
-        us += ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + row + 8) * 16 + col) * 4));
-      }
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1) {
+          gs += tg[s];
+          us += tu[s];
+        }
       const float a = gs / (1.f + __expf(-gs)) * us;
       stc2(rs_as, (uint32_t)(col * Is + sb * 8 + row) * 2u, f2bf(a));
     }
@@ -711,14 +740,49 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   // order; a round takes the wave-wide largest head, which on equal keys is the
   // lowest lane and within it the lowest j: the lower expert id ("glm53:
   // Long-context indexer ...", PR 85 commit row 9: ID order on ties)
-  if (!wait_cnt<false>(p, bk, &bk->router[0], 16, 1, (uint32_t)n_rb, false, &S.flags[2], 1, ep, 0)) return;
+  // With few rows x chunks, each workgroup sums the router chunks itself (in
+  // chunk order, the same sums as above) into LDS: no last-arriver hop.
+  float* const lgs = (float*)&S.red[0][0][0];  // [R][E]; the reduction tiles are idle here
+  if constexpr (RS) {
+    if (!wait_cnt<true>(p, bk, &bk->unitc[0][0], 16, n_rb, (uint32_t)(n_rb * S1), false, &S.flags[2], 1, ep, 0))
+      return;
+    const int E4 = (E + 3) >> 2;
+    for (int q = tid; q < R * E4; q += NT) {  // 4 experts of one row per thread
+      const int r = q / E4, e = 4 * (q - r * E4), u = e >> 4, row = e & 15;
+      u32x4 t[NQ];
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1) t[s] = ld16<CP_SC1>(rs_pt, (uint32_t)((((u * S1 + s) * 16 + r) * 16 + row) * 4));
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] += __uint_as_float(t[s][j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e + j < E) lgs[r * E + e + j] = v[j];
+    }
+    __syncthreads();
+  } else if (!wait_cnt<false>(p, bk, &bk->router[0], 16, 1, (uint32_t)n_rb, false, &S.flags[2], 1, ep, 0)) {
+    return;
+  }
   TL(5);
   for (int r = wave; r < R; r += NW) {
     const int e0 = 8 * lane;
-    const u32x4 la = ld16<CP_SC1>(rs_lg, e0 < E ? (uint32_t)(r * p.Ep + e0) * 4u : OOB);
-    const u32x4 lb = ld16<CP_SC1>(rs_lg, e0 + 4 < E ? (uint32_t)(r * p.Ep + e0 + 4) * 4u : OOB);
-    const float lg[8] = {__uint_as_float(la[0]), __uint_as_float(la[1]), __uint_as_float(la[2]), __uint_as_float(la[3]),
-                         __uint_as_float(lb[0]), __uint_as_float(lb[1]), __uint_as_float(lb[2]), __uint_as_float(lb[3])};
+    float lg[8];
+    if constexpr (RS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lg[j] = e0 + j < E ? lgs[r * E + e0 + j] : 0.f;
+    } else {
+      const u32x4 la = ld16<CP_SC1>(rs_lg, e0 < E ? (uint32_t)(r * p.Ep + e0) * 4u : OOB);
+      const u32x4 lb = ld16<CP_SC1>(rs_lg, e0 + 4 < E ? (uint32_t)(r * p.Ep + e0 + 4) * 4u : OOB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lg[j] = __uint_as_float(la[j]);
+        lg[4 + j] = __uint_as_float(lb[j]);
+      }
+    }
     uint64_t qv[8];
     if (p.scoring == MOE_TAIL_SOFTMAX) {
 #pragma unroll
@@ -827,8 +891,11 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       if (p.topk_ids) p.topk_ids[q] = S.ids[q];
       if (p.topk_w) p.topk_w[q] = S.w[q];
     }
-    if (p.dbg_logits)
-      for (int q = tid; q < R * E; q += NT) p.dbg_logits[q] = ldcf(rs_lg, (uint32_t)((q / E) * p.Ep + q % E) * 4u);
+    if (p.dbg_logits) {
+      for (int q = tid; q < R * E; q += NT)
+        p.dbg_logits[q] = RS ? lgs[q] : ldcf(rs_lg, (uint32_t)((q / E) * p.Ep + q % E) * 4u);
+      if (RS) __syncthreads();  // the routed phase reuses these LDS tiles
+    }
   }
   TL(7);
 
@@ -1168,13 +1235,27 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   TL(12);
 }
 
-__global__ __launch_bounds__(NT, 1) void moe_tail_kernel(Params p) {
+// Separate kernels rather than run-time branches, so that each launch's code
+// is compact: activations staged in LDS, or read from global scratch (wide
+// rows); router sums by the last chunk's workgroup, or by every reader.
+__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_lds(Params p) {
   __shared__ Shared S;
   extern __shared__ __attribute__((aligned(16))) char s_dyn[];
-  if (p.xn_lds)
-    tail<true>(p, S, s_dyn);
-  else
-    tail<false>(p, S, s_dyn);
+  tail<true, false>(p, S, s_dyn);
+}
+__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_lds_rs(Params p) {
+  __shared__ Shared S;
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  tail<true, true>(p, S, s_dyn);
+}
+__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_gm(Params p) {
+  __shared__ Shared S;
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  tail<false, false>(p, S, s_dyn);
+}
+static const void* kernel_for(const Params& p) {
+  if (!p.xn_lds) return (const void*)moe_tail_kernel_gm;
+  return p.rsum ? (const void*)moe_tail_kernel_lds_rs : (const void*)moe_tail_kernel_lds;
 }
 
 }  // namespace mt
@@ -1290,7 +1371,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
   const int G = prop.multiProcessorCount;
   hipFuncAttributes fa;
-  HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel));
+  HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel_lds));
   if (G > mt::MAX_G) return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d compute units, at most %d supported", G, mt::MAX_G);
   const int S1 = chunks_per_block(cfg->hidden, cfg->num_experts, G), TC = cfg->hidden / 32 / S1;
   const int n_rb = (cfg->num_experts + 15) / 16, n_sb = cfg->shared_inter / 8;
@@ -1341,7 +1422,11 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   }
   e = hipMemset(h->scratch, 0, total);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)mt::moe_tail_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    e = hipFuncSetAttribute(plan.xn_lds ? (const void*)mt::moe_tail_kernel_lds : (const void*)mt::moe_tail_kernel_gm,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  if (e == hipSuccess && plan.xn_lds)
+    e = hipFuncSetAttribute((const void*)mt::moe_tail_kernel_lds_rs, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)dyn);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) {
@@ -1397,6 +1482,8 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.scoring = c.scoring;
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
+  // reader-side router sums when each thread then loads at most 8 partials
+  p.rsum = p.xn_lds && rows * c.num_experts * h->S1 <= 8192 && rows * c.num_experts <= mt::RED_FLOATS;
   p.xs = h->plan.xs;
   p.cs = h->plan.cs;
   p.n_rb = h->n_rb;
@@ -1445,33 +1532,49 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   HIPCHK(h, hipStreamIsCapturing(s, &cs));
   void* kargs[] = {&p};
+  const void* kern = mt::kernel_for(p);
   hipError_t e;
   if (cs == hipStreamCaptureStatusNone)
-    e = hipLaunchCooperativeKernel((const void*)mt::moe_tail_kernel, dim3(h->G), dim3(mt::NT), kargs,
+    e = hipLaunchCooperativeKernel(kern, dim3(h->G), dim3(mt::NT), kargs,
                                    (unsigned)h->lds_dyn, s);
   else
-    e = hipLaunchKernel((const void*)mt::moe_tail_kernel, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, s);
+    e = hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, s);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "kernel launch: %s", hipGetErrorString(e));
   return MOE_TAIL_OK;
 }
 
 extern "C" moe_tail_status moe_tail_get_error(moe_tail_t* h) {
   if (!h) return fail(nullptr, MOE_TAIL_EINVAL, "handle is NULL");
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint32_t w[8] = {0};
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->device);
-  hipError_t e = hipMemcpy(w, &h->ctl->error, sizeof(w), hipMemcpyDeviceToHost);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(w, &h->ctl->error, sizeof(w), hipMemcpyDeviceToHost);
   const uint32_t v = w[0];
-  if (e == hipSuccess && v) e = hipMemset(&h->ctl->error, 0, sizeof(w));
+  uint32_t ep_lo = 0, ep_hi = 0;
+  if (e == hipSuccess && v) {  // the workgroups' epochs, for the message
+    static_assert(sizeof(mt::Ctl::cta_ep[0]) == 64, "one line per workgroup");
+    std::vector<uint32_t> eps((size_t)h->G * 16);
+    e = hipMemcpy(eps.data(), h->ctl->cta_ep, eps.size() * 4, hipMemcpyDeviceToHost);
+    ep_lo = ep_hi = eps[0];
+    for (int i = 1; i < h->G; ++i) {
+      ep_lo = eps[i * 16] < ep_lo ? eps[i * 16] : ep_lo;
+      ep_hi = eps[i * 16] > ep_hi ? eps[i * 16] : ep_hi;
+    }
+  }
+  // after a failed call the workgroups' epochs and counters may disagree:
+  // start the handle's control block over (nothing is in flight now)
+  if (e == hipSuccess && v) e = hipMemset(h->ctl, 0, sizeof(mt::Ctl));
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "reading the error word: %s", hipGetErrorString(e));
   static const char* names[4] = {"norm", "router", "shared", "routed"};
   if (v == MOE_TAIL_ETIMEOUT)
     return fail(h, MOE_TAIL_ETIMEOUT,
-                "a cross-workgroup wait passed its deadline: %s wait in workgroup %u saw %u of %u (epoch %u, %u slots)",
-                w[1] < 4 ? names[w[1]] : "?", w[2], w[3], w[4], w[5], w[6]);
+                "a cross-workgroup wait passed its deadline: %s wait in workgroup %u saw %u of %u (epoch %u, info %u; "
+                "workgroup epochs now %u..%u)",
+                w[1] < 4 ? names[w[1]] : "?", w[2], w[3], w[4], w[5], w[6], ep_lo, ep_hi);
   return MOE_TAIL_OK;
 }
 

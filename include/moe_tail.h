@@ -113,8 +113,10 @@ moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
 moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_tail_args* args, void* stream);
 
 /* Read and clear the sticky device error word (MOE_TAIL_OK or
- * MOE_TAIL_ETIMEOUT).  Synchronous; call after the caller has synchronised
- * the stream of the runs it covers. */
+ * MOE_TAIL_ETIMEOUT).  Synchronises the device first.  While the word is set,
+ * later calls on the handle give up at their first wait that is not already
+ * satisfied (their outputs are then undefined); reading an error also resets
+ * the handle's call epochs and counters, so the next call starts clean. */
 moe_tail_status moe_tail_get_error(moe_tail_t* h);
 
 /* Text of the last error reported on this handle (or on creation when h is
