@@ -136,9 +136,10 @@ class Workload:
                         self.call(i, s)
             graphs.append((n, g))
         big = graphs[0][1]
-        for _ in range(max(1, warmup // per_graph)):
-            big.replay()
-        s.synchronize()
+        with t.cuda.stream(s):  # same stream as the timed replays: calls on one handle never overlap
+            for _ in range(max(1, warmup // per_graph)):
+                big.replay()
+        t.cuda.synchronize()
         e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         e0.record(s)
         with t.cuda.stream(s):
@@ -165,6 +166,8 @@ class Workload:
             self.call(i, s)
         e1.record(s)
         s.synchronize()
+        if self.h.get_error() != binding.OK:
+            raise RuntimeError("device error during timing: " + binding.strerror(self.h.h))
         return e0.elapsed_time(e1) * 1e3 / steps
 
     def eager_us(self, reps=20):
