@@ -945,9 +945,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const uint32_t qoff = (uint32_t)(wrow * (H / 2) + g * 16), soff = (uint32_t)(wrow * (H / 32) + tb * 4);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (t < np) f.a[t] = ld16<CP_W>(rq, (v && tb + t < T2) ? qoff + (uint32_t)(tb + t) * 64u : OOB);
+          f.a[t] = ld16<CP_W>(rq, (v && t < np && tb + t < T2) ? qoff + (uint32_t)(tb + t) * 64u : OOB);
         f.s[0] = ld16<CP_W>(rs, v ? soff : OOB);
-        if (np > 4) f.s[1] = ld16<CP_W>(rs, v ? soff + 16u : OOB);
+        f.s[1] = ld16<CP_W>(rs, (v && np > 4) ? soff + 16u : OOB);
         if (++q2 == NP) {
           q2 = 0;
           ++k2;
