@@ -155,6 +155,16 @@ constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
+// The same for a base and size that are uniform but that the compiler may keep
+// in vector registers: read from the first lane, so the load needs no
+// per-lane descriptor loop.
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), nb);
+}
 template <int CP>
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP));
@@ -421,9 +431,9 @@ struct FragQB {
   uint32_t s;
   u32x4 b[4];
 };
-struct FragD {  // MXFP4 down: up to 4 column groups x both row blocks, with their block scales
-  u32x4 a[4][MAX_BLK];
-  u32x4 s[MAX_BLK];
+struct FragD {  // MXFP4 down: 2 column groups x both row blocks, with the dwords holding their block scales
+  u32x4 a[2][MAX_BLK];
+  uint32_t s[MAX_BLK][2];
 };
 struct FragSD {
   u32x4 a[MAX_BLK];
@@ -1049,44 +1059,29 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   float* s_outp = (float*)(dyn + p.off_outp);   // [P][HR]
   float* s_shp = (float*)(dyn + p.off_shp);     // [NW][R][HR]
   const int azero = p.azero, szero = p.szero;
-  // source: frags of up to 4 column groups (of 128 I-elements) of slot j3 (slot
-  // d = wave + NW * j3), both 16-row blocks, with their block scales: when the
-  // scale rows are whole dwords, one 16-byte load per block gives lane (i16, g)
-  // dwords 4 q3 .. 4 q3 + 3 of its row (column group 4 q3 + t uses dword t, byte
-  // g); otherwise one byte per column group.
-  const int NP3 = (TI + 3) / 4;
-  const bool s4 = (CI & 3) == 0;
+  // source: frags of 2 column groups (of 128 I-elements) of slot j3 (slot
+  // d = wave + NW * j3), both 16-row blocks, with their block scales: lane
+  // (i16, g) needs scale byte 4 t3 + g of its row for column group t3, and
+  // loads the dword that holds it.  Every load is issued (out-of-range ones
+  // read zero without a memory access), so the compiler counts them exactly.
+  const int NP3 = (TI + 1) / 2;
   int j3 = 0, q3 = 0;
   auto p3_next = [&]() {
     FragD f;
     const bool v = j3 < nsl && hn > 0;
     const int e = v ? __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]) : 0;  // uniform
-    const rsrc_t rq = make_rsrc(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
-    const rsrc_t rs = make_rsrc(p.w2s + e * S2s + (size_t)h0 * CI, (uint32_t)(hn * CI));
+    const size_t so = (size_t)e * S2s + (size_t)h0 * CI;  // scale slice start; the dword loads stay inside the array
+    const rsrc_t rq = make_rsrc_u(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
+    const rsrc_t rs = make_rsrc_u(p.w2s + so, (uint32_t)((size_t)E * H * CI - so));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int t3 = 4 * q3 + t, c = 4 * t3 + g;
-      if (t3 < TI) {
+    for (int t = 0; t < 2; ++t) {
+      const int t3 = 2 * q3 + t, c = 4 * t3 + g;
 #pragma unroll
-        for (int bl = 0; bl < MAX_BLK; ++bl) {
-          const int hh = 16 * bl + i16;
-          if (bl < nblk) f.a[t][bl] = ld16<CP_W>(rq, (v && hh < hn && c < CI) ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
-        }
-      }
-    }
-#pragma unroll
-    for (int bl = 0; bl < MAX_BLK; ++bl) {
-      const int hh = 16 * bl + i16;
-      if (bl < nblk) {
-        if (s4) {
-          f.s[bl] = ld16<CP_W>(rs, (v && hh < hn) ? (uint32_t)(hh * CI + 16 * q3) : OOB);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int t3 = 4 * q3 + t, c = 4 * t3 + g;
-            f.s[bl][t] = ld1<CP_W>(rs, (v && hh < hn && c < CI) ? (uint32_t)(hh * CI + c) : OOB);
-          }
-        }
+      for (int bl = 0; bl < MAX_BLK; ++bl) {
+        const int hh = 16 * bl + i16;
+        const bool ok = v && t3 < TI && bl < nblk && hh < hn && c < CI;
+        f.a[t][bl] = ld16<CP_W>(rq, ok ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
+        f.s[bl][t] = ld4<CP_W>(rs, ok ? (uint32_t)(hh * CI + c) & ~3u : OOB);
       }
     }
     if (++q3 == NP3) {
@@ -1183,8 +1178,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
       const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int t3 = 4 * qu + t, c = 4 * t3 + g;
+      for (int t = 0; t < 2; ++t) {
+        const int t3 = 2 * qu + t, c = 4 * t3 + g;
         if (t3 < TI) {
           u32x4 b[4];
 #pragma unroll
@@ -1192,7 +1187,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
           for (int bl = 0; bl < MAX_BLK; ++bl) {
             if (bl < nblk) {
-              const uint32_t sb = s4 ? (f.s[bl][t] >> (8 * g)) : f.s[bl][t];
+              const uint32_t sb = f.s[bl][t] >> (8 * (((16 * bl + i16) * CI + c) & 3));
               const float sc = e8m0f(sb & 0xFFu);
 #pragma unroll
               for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[t][bl][q], sc), as_bf16x8(b[q]), acc[bl]);
