@@ -1065,14 +1065,18 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   // loads the dword that holds it.  Every load is issued (out-of-range ones
   // read zero without a memory access), so the compiler counts them exactly.
   const int NP3 = (TI + 1) / 2;
+  const int s3r = (h0 * CI) & 3;  // slice start mod 4 (expert strides H CI are multiples of 4)
   int j3 = 0, q3 = 0;
   auto p3_next = [&]() {
     FragD f;
     const bool v = j3 < nsl && hn > 0;
     const int e = v ? __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]) : 0;  // uniform
-    const size_t so = (size_t)e * S2s + (size_t)h0 * CI;  // scale slice start; the dword loads stay inside the array
+    // scale bytes from a 4-byte aligned base at or below the slice start; the
+    // dword loads stay inside the array (its size is a multiple of 4)
+    const size_t so = (size_t)e * S2s + (size_t)h0 * CI, sa = so & ~(size_t)3;
+    const uint32_t sr = (uint32_t)(so - sa);
     const rsrc_t rq = make_rsrc_u(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
-    const rsrc_t rs = make_rsrc_u(p.w2s + so, (uint32_t)((size_t)E * H * CI - so));
+    const rsrc_t rs = make_rsrc_u(p.w2s + sa, (uint32_t)((size_t)E * H * CI - sa));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int t3 = 2 * q3 + t, c = 4 * t3 + g;
@@ -1081,7 +1085,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const int hh = 16 * bl + i16;
         const bool ok = v && t3 < TI && bl < nblk && hh < hn && c < CI;
         f.a[t][bl] = ld16<CP_W>(rq, ok ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
-        f.s[bl][t] = ld4<CP_W>(rs, ok ? (uint32_t)(hh * CI + c) & ~3u : OOB);
+        f.s[bl][t] = ld4<CP_W>(rs, ok ? (sr + (uint32_t)(hh * CI + c)) & ~3u : OOB);
       }
     }
     if (++q3 == NP3) {
@@ -1187,7 +1191,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
           for (int bl = 0; bl < MAX_BLK; ++bl) {
             if (bl < nblk) {
-              const uint32_t sb = f.s[bl][t] >> (8 * (((16 * bl + i16) * CI + c) & 3));
+              const uint32_t sb = f.s[bl][t] >> (8 * ((s3r + (16 * bl + i16) * CI + c) & 3));
               const float sc = e8m0f(sb & 0xFFu);
 #pragma unroll
               for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[t][bl][q], sc), as_bf16x8(b[q]), acc[bl]);

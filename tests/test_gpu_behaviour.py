@@ -111,3 +111,24 @@ def test_deadline_fault_drill_then_recovery():
     g = run(good, cfg, dw, x, r)
     assert good.get_error() == binding.OK
     check_against_oracle(g, o, cfg)
+
+
+def test_calls_after_a_timeout_fail_fast_until_the_error_is_read():
+    """After a deadline fires, later calls on the handle give up at their first
+    unmet wait instead of waiting out a deadline each; reading the error
+    reports the failed wait and resets the handle's control block."""
+    import time
+
+    cfg = synth.CONFIGS["c0"]
+    w = weights("c0")
+    x, r, _ = gapped_rows(cfg, w)
+    dw = device_weights("c0")
+    bad = handle_for(cfg, deadline_us=50000, debug_flags=binding.DEBUG_STALL, debug_block=3)
+    run(bad, cfg, dw, x, r)  # times out after 50 ms
+    t0 = time.perf_counter()
+    for _ in range(5):
+        run(bad, cfg, dw, x, r)  # the error word is still set: these exit at once
+    assert (time.perf_counter() - t0) < 0.2, "calls after a timeout waited out their deadlines"
+    assert bad.get_error() == binding.ETIMEOUT
+    msg = binding.strerror(bad.h)
+    assert "deadline" in msg and "epochs" in msg, msg
