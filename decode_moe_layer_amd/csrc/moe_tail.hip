@@ -130,8 +130,9 @@ struct Params {
   float* dbg_ys;
   Ctl* ctl;
   uint16_t* xn;
-  float* logits;
-  float* part1;  // [blocks * S1][16][16] fp32 K-chunk partial sums
+  uint64_t* xnt;    // [R][H/2] tagged xn pairs (this call's K-chunk readers)
+  uint64_t* lgt;    // [R][Ep] tagged fp32 logits
+  uint64_t* part1;  // [blocks * S1][16][16] tagged fp32 K-chunk partial sums
   uint16_t* a_s;
   uint16_t* a_r;
 };
@@ -176,9 +177,6 @@ __device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) {
 template <int CP>
 __device__ __forceinline__ uint32_t ld1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, CP);
-}
-__device__ __forceinline__ float ldcf(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP_SC1));
 }
 __device__ __forceinline__ void stc16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
@@ -321,6 +319,53 @@ struct Window {
 
 // -------------------------------------------------------- cross-CTA sync --
 
+// Tagged words: a 32-bit payload with the call's epoch in the high half,
+// stored and loaded as one 64-bit device-scope atomic.  A reader that finds
+// this call's epoch in every word it needs has its data, with no separate
+// flag, fence or counter between the writer and it.  Epochs only grow (the
+// scratch is cleared whenever they restart), so a word from an earlier call
+// never carries this call's tag.
+__device__ __forceinline__ void st_tag(uint64_t* w, uint32_t v, uint32_t ep) {
+  __hip_atomic_store(w, ((uint64_t)ep << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* w) {
+  return __hip_atomic_load(const_cast<uint64_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t ep) { return (uint32_t)(w >> 32) == ep; }
+// Two tagged words in one 16-byte device-scope load ({payload, tag, payload,
+// tag}); each word carries its own tag, and an aligned 16-byte access is
+// never split below 8 bytes.
+__device__ __forceinline__ u32x4 ld_tag2(rsrc_t r, uint32_t word) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(word * 8u), 0, CP_SC1));
+}
+
+// Whether a wave polling since t0 gives up (wave-uniform): this call was
+// aborted, an earlier call's error is unread (a handle in error fails fast
+// instead of waiting out one deadline per call), or this wait passed its
+// deadline, which aborts the call and records the first timeout.
+__device__ __forceinline__ bool give_up(const Params& p, Bank* bk, unsigned long long t0, uint32_t wait_id,
+                                        uint32_t seen, uint32_t target, uint32_t ep, uint32_t info) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ab = 0;
+  if (lane == 0) ab = __hip_atomic_load(&bk->abort_[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 1) ab = __hip_atomic_load(&p.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__ballot(ab != 0u)) return true;
+  if (wall_clock64() - t0 > p.deadline_ticks) {
+    if (lane == 0) {
+      __hip_atomic_fetch_or(&bk->abort_[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t zero = 0;
+      if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        const uint32_t d[6] = {wait_id, blockIdx.x, seen, target, ep, info};
+        for (int k = 0; k < 6; ++k)
+          __hip_atomic_store(&p.ctl->diag[k], d[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return true;
+  }
+  return false;
+}
+
 // Wait until this workgroup's (SC1) stores have completed, then add n to *c.
 __device__ __forceinline__ void publish(uint32_t* c, uint32_t n) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -361,27 +406,7 @@ __device__ __forceinline__ bool wait_cnt(const Params& p, Bank* bk, const uint32
         seen = done ? target : (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
       }
       if (done && !stall) break;
-      // this call's abort word, and the sticky error of an earlier call that
-      // has not been read yet: a handle in error fails fast instead of
-      // waiting out one deadline per call
-      uint32_t ab = 0;
-      if (lane == 0) ab = __hip_atomic_load(&bk->abort_[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (lane == 1) ab = __hip_atomic_load(&p.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__ballot(ab != 0u)) {
-        ok = 0;
-        break;
-      }
-      if (wall_clock64() - t0 > p.deadline_ticks) {
-        if (lane == 0) {
-          __hip_atomic_fetch_or(&bk->abort_[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          uint32_t zero = 0;
-          if (__hip_atomic_compare_exchange_strong(&p.ctl->error, &zero, (uint32_t)MOE_TAIL_ETIMEOUT, __ATOMIC_RELAXED,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            const uint32_t d[6] = {wait_id, blockIdx.x, seen, target, ep, info};
-            for (int k = 0; k < 6; ++k)
-              __hip_atomic_store(&p.ctl->diag[k], d[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
+      if (give_up(p, bk, t0, wait_id, seen, target, ep, info)) {
         ok = 0;
         break;
       }
@@ -473,8 +498,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int n_rb = p.n_rb, n_sb = p.n_sb, S1 = p.S1, TC = p.TC;
   const int n_it = (n_rb + n_sb) * S1;
   const rsrc_t rs_xn = make_rsrc(p.xn, (uint32_t)(R * H * 2));
-  const rsrc_t rs_lg = make_rsrc(p.logits, (uint32_t)(R * p.Ep * 4));
-  const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * 1024));
+  const rsrc_t rs_xt = make_rsrc(p.xnt, (uint32_t)(R * H * 4));
+  const rsrc_t rs_lt = make_rsrc(p.lgt, (uint32_t)(R * p.Ep * 8));
+  const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * 2048));
   const rsrc_t rs_as = make_rsrc(p.a_s, (uint32_t)(R * Is * 2));
   const rsrc_t rs_ar = make_rsrc(p.a_r, (uint32_t)(P * I * 2));
   uint16_t* xl = (uint16_t*)dyn;  // [xrows][xs] staged activations; row xzero is zeros
@@ -494,6 +520,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     epv = __hip_atomic_fetch_add(&p.ctl->cta_ep[cta][z], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid < E) S.rowmask[tid] = 0u;
+  if (tid == 0) S.flags[5] = 0u;  // set by a top-k wave whose logits poll gave up
   const bool stall = (p.debug_flags & MOE_TAIL_DEBUG_STALL) && cta == p.debug_block;
 
   // ---- router/shared source.  Item i = cta, cta + G, ... is K chunk i % S1 of
@@ -568,7 +595,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     ss = wave_sum_f64(ss);
     if (lane == 0) S.tmpd[wave] = ss;
+    if (tid == 0) S.ep = epv + 1u;  // the epoch atomic went out before the row loads
     __syncthreads();
+    const uint32_t epn = S.ep;
     double tot = 0.0;
     for (int w = 0; w < NW; ++w) tot += S.tmpd[w];
     const double rstd = 1.0 / sqrt(tot / (double)H + p.eps);
@@ -584,6 +613,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         nv[c] = n0 | (n1 << 16);
       }
       stc16(rs_xn, (uint32_t)(row * H + i) * 2u, nv);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st_tag(p.xnt + (size_t)(row * H + i) / 2 + c, nv[c], epn);
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
     }
   }
@@ -606,26 +637,40 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   }
   TL(1);
 
-  // ---- router/shared phase: stage this chunk of xn, then the items' MFMA tiles
+  // Workgroup-uniform poll: attempt() loads tagged words, keeps their payloads
+  // and reports whether all of this thread's words carry this call's tag; it
+  // is repeated until every thread's do.  False when the call is aborted.
+  auto poll_all = [&](auto attempt, uint32_t wait_id, uint32_t info, bool stl) -> bool {
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+      const bool ok = attempt();
+      if (__syncthreads_and(ok && !stl)) return true;
+      if (tid < 64) {
+        const bool gu = give_up(p, bk, t0, wait_id, 0u, 1u, ep, info);
+        if (tid == 0) S.flags[6] = gu;
+      }
+      __syncthreads();
+      if (S.flags[6]) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+
+  // ---- router/shared phase: stage this chunk of xn (tagged words written by
+  // the norm workgroups), then the items' MFMA tiles
   if (nu1) {
-    if (!wait_cnt<false>(p, bk, &bk->normc[s1 * (NQ / S1)][0], 16, NQ / S1, (uint32_t)R, stall, &S.flags[0], 0, ep,
-                         0))
+    const int CW = TC * 32, pr = CW / 4, np2 = R * pr;  // word pairs per row, in all
+    if (!poll_all([&]() {
+          bool ok = true;
+          for (int w = tid; w < np2; w += NT) {
+            const int r = w / pr, c = w - r * pr;
+            const u32x4 v = ld_tag2(rs_xt, (uint32_t)(r * (H / 2) + s1 * (CW / 2) + 2 * c));
+            ok = ok && v[1] == ep && v[3] == ep;
+            *(uint2*)(xc + r * p.cs + 4 * c) = make_uint2(v[0], v[2]);
+          }
+          return ok;
+        }, 0, 0, stall))
       return;
     TL(2);
-    const int CW = TC * 32, c8n = CW / 8, n8 = R * c8n;
-    for (int base = 0; base < n8; base += NT * 8) {
-      u32x4 v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e8 = base + k * NT + tid, r = e8 / c8n, c8 = e8 - r * c8n;
-        v[k] = ld16<CP_SC1>(rs_xn, e8 < n8 ? (uint32_t)(r * H + s1 * CW + c8 * 8) * 2u : OOB);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e8 = base + k * NT + tid, r = e8 / c8n, c8 = e8 - r * c8n;
-        if (e8 < n8) *(u32x4*)(xc + r * p.cs + c8 * 8) = v[k];
-      }
-    }
     for (int c = tid * 8; c < p.cs; c += NT * 8) *(u32x4*)(xc + xzero * p.cs + c) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
   }
@@ -650,7 +695,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           float v = 0.f;
           for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
           const int row = 4 * (l >> 4) + qq, col = l & 15;
-          if (col < R) stcf(rs_pt, (uint32_t)((it * 16 + col) * 16 + row) * 4u, v);
+          if (col < R) st_tag(p.part1 + (it * 16 + col) * 16 + row, __float_as_uint(v), ep);
         }
         rb ^= 1;
       }
@@ -675,17 +720,17 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         float t[NQ];
 #pragma unroll
         for (int s = 0; s < NQ; ++s)
-          if (s < S1) t[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row) * 4));
+          if (s < S1) t[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
         float v = 0.f;
 #pragma unroll
         for (int s = 0; s < NQ; ++s)
           if (s < S1) v += t[s];
         const int e = u * 16 + row;
-        if (e < E) stcf(rs_lg, (uint32_t)(col * p.Ep + e) * 4u, v);
+        if (e < E) st_tag(p.lgt + col * p.Ep + e, __float_as_uint(v), ep);
       }
       ++nr;
     }
-    if (nr) publish(&bk->router[0], (uint32_t)nr);
+    (void)nr;
     // shared blocks: a = silu(gate) * up over the chunks summed in chunk order,
     // all of this workgroup's blocks at once (one round trip for the partials)
     if (tid == 0) {
@@ -705,8 +750,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
       for (int s = 0; s < NQ; ++s)
         if (s < S1) {
-          tg[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row) * 4));
-          tu[s] = ldcf(rs_pt, (uint32_t)((((u * S1 + s) * 16 + col) * 16 + row + 8) * 4));
+          tg[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
+          tu[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row + 8));
         }
       float gs = 0.f, us = 0.f;
 #pragma unroll
@@ -754,28 +799,33 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   // chunk order, the same sums as above) into LDS: no last-arriver hop.
   float* const lgs = (float*)&S.red[0][0][0];  // [R][E]; the reduction tiles are idle here
   if constexpr (RS) {
-    if (!wait_cnt<true>(p, bk, &bk->unitc[0][0], 16, n_rb, (uint32_t)(n_rb * S1), false, &S.flags[2], 1, ep, 0))
-      return;
     const int E4 = (E + 3) >> 2;
-    for (int q = tid; q < R * E4; q += NT) {  // 4 experts of one row per thread
-      const int r = q / E4, e = 4 * (q - r * E4), u = e >> 4, row = e & 15;
-      u32x4 t[NQ];
+    if (!poll_all([&]() {
+          bool ok = true;
+          for (int q = tid; q < R * E4; q += NT) {  // 4 experts of one row per thread
+            const int r = q / E4, e = 4 * (q - r * E4), u = e >> 4, row = e & 15;
+            u32x4 t[NQ][2];
 #pragma unroll
-      for (int s = 0; s < NQ; ++s)
-        if (s < S1) t[s] = ld16<CP_SC1>(rs_pt, (uint32_t)((((u * S1 + s) * 16 + r) * 16 + row) * 4));
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < NQ; ++s)
+              if (s < S1)
 #pragma unroll
-      for (int s = 0; s < NQ; ++s)
-        if (s < S1)
+                for (int j = 0; j < 2; ++j) t[s][j] = ld_tag2(rs_pt, (uint32_t)(((u * S1 + s) * 16 + r) * 16 + row + 2 * j));
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] += __uint_as_float(t[s][j]);
+            for (int s = 0; s < NQ; ++s)
+              if (s < S1)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e + j < E) lgs[r * E + e + j] = v[j];
-    }
-    __syncthreads();
-  } else if (!wait_cnt<false>(p, bk, &bk->router[0], 16, 1, (uint32_t)n_rb, false, &S.flags[2], 1, ep, 0)) {
-    return;
+                for (int j = 0; j < 4; ++j) {
+                  ok = ok && t[s][j >> 1][2 * (j & 1) + 1] == ep;
+                  v[j] += __uint_as_float(t[s][j >> 1][2 * (j & 1)]);
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (e + j < E) lgs[r * E + e + j] = v[j];
+          }
+          return ok;
+        }, 1, 0, false))
+      return;
   }
   TL(5);
   for (int r = wave; r < R; r += NW) {
@@ -784,13 +834,29 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     if constexpr (RS) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) lg[j] = e0 + j < E ? lgs[r * E + e0 + j] : 0.f;
-    } else {
-      const u32x4 la = ld16<CP_SC1>(rs_lg, e0 < E ? (uint32_t)(r * p.Ep + e0) * 4u : OOB);
-      const u32x4 lb = ld16<CP_SC1>(rs_lg, e0 + 4 < E ? (uint32_t)(r * p.Ep + e0 + 4) * 4u : OOB);
+    } else {  // this row's tagged logits, polled by this wave alone
+      const unsigned long long t0 = wall_clock64();
+      bool failed = false;
+      for (;;) {
+        bool ok = true;
+        u32x4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lg[j] = __uint_as_float(la[j]);
-        lg[4 + j] = __uint_as_float(lb[j]);
+        for (int j = 0; j < 4; ++j) v[j] = ld_tag2(rs_lt, e0 < E ? (uint32_t)(r * p.Ep + e0 + 2 * j) : OOB / 8u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          ok = ok && (e0 + j >= E || v[j >> 1][2 * (j & 1) + 1] == ep);
+          lg[j] = __uint_as_float(v[j >> 1][2 * (j & 1)]);
+        }
+        if (__ballot(!ok) == 0) break;
+        if (give_up(p, bk, t0, 1, 0u, 1u, ep, (uint32_t)r)) {
+          failed = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (failed) {
+        if (lane == 0) S.flags[5] = 1u;
+        continue;
       }
     }
     uint64_t qv[8];
@@ -852,6 +918,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
   }
   __syncthreads();
+  if (S.flags[5]) return;  // a logits poll gave up: the call is aborted
   TL(6);
 
   // ---- de-duplication: one slot per distinct expert, in expert order, with
@@ -903,7 +970,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     if (p.dbg_logits) {
       for (int q = tid; q < R * E; q += NT)
-        p.dbg_logits[q] = RS ? lgs[q] : ldcf(rs_lg, (uint32_t)((q / E) * p.Ep + q % E) * 4u);
+        p.dbg_logits[q] = RS ? lgs[q] : __uint_as_float((uint32_t)ld_tag(p.lgt + (q / E) * p.Ep + q % E));
       if (RS) __syncthreads();  // the routed phase reuses these LDS tiles
     }
   }
@@ -1311,8 +1378,10 @@ struct moe_tail {
   void* scratch;
   mt::Ctl* ctl;
   uint16_t* xn;
-  float* logits;
-  float* part1;
+  uint64_t* xnt;
+  uint64_t* lgt;
+  uint64_t* part1;
+  size_t scratch_bytes;
   uint16_t* a_s;
   uint16_t* a_r;
   int S1, TC, n_rb, n_sb, Ep;
@@ -1406,8 +1475,9 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   const size_t R = cfg->max_rows, H = cfg->hidden, E = cfg->num_experts, K = cfg->top_k;
   const size_t I = cfg->inter, Is = cfg->shared_inter;
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
-  const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_lg = o_xn + al(R * H * 2);
-  const size_t o_pt = o_lg + al(R * (size_t)h->Ep * 4), o_as = o_pt + al((size_t)n_it * 1024);
+  const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_xnt = o_xn + al(R * H * 2);
+  const size_t o_lg = o_xnt + al(R * H * 4), o_pt = o_lg + al(R * (size_t)h->Ep * 8);
+  const size_t o_as = o_pt + al((size_t)n_it * 2048);
   const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
   (void)E;
   int prev = 0;
@@ -1436,8 +1506,10 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   char* base = (char*)h->scratch;
   h->ctl = (mt::Ctl*)(base + o_ctl);
   h->xn = (uint16_t*)(base + o_xn);
-  h->logits = (float*)(base + o_lg);
-  h->part1 = (float*)(base + o_pt);
+  h->xnt = (uint64_t*)(base + o_xnt);
+  h->lgt = (uint64_t*)(base + o_lg);
+  h->part1 = (uint64_t*)(base + o_pt);
+  h->scratch_bytes = total;
   h->a_s = (uint16_t*)(base + o_as);
   h->a_r = (uint16_t*)(base + o_ar);
   snprintf(h->err, sizeof(h->err), "no error");
@@ -1522,7 +1594,8 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.dbg_ys = a->dbg_y_shared;
   p.ctl = h->ctl;
   p.xn = h->xn;
-  p.logits = h->logits;
+  p.xnt = h->xnt;
+  p.lgt = h->lgt;
   p.part1 = h->part1;
   p.a_s = h->a_s;
   p.a_r = h->a_r;
@@ -1563,8 +1636,9 @@ extern "C" moe_tail_status moe_tail_get_error(moe_tail_t* h) {
     }
   }
   // after a failed call the workgroups' epochs and counters may disagree:
-  // start the handle's control block over (nothing is in flight now)
-  if (e == hipSuccess && v) e = hipMemset(h->ctl, 0, sizeof(mt::Ctl));
+  // start the handle's scratch over (nothing is in flight now).  The epochs
+  // restart, so the tagged words are cleared with them.
+  if (e == hipSuccess && v) e = hipMemset(h->scratch, 0, h->scratch_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "reading the error word: %s", hipGetErrorString(e));
