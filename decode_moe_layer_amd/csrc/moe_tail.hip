@@ -75,11 +75,11 @@ constexpr int MAX_ITEMS1 = 64;     // K-chunk items of the router/shared phase p
 
 // Arrival counters of one call.  Every counter sits on its own 64-byte line;
 // contention on one address serialises the atomics, so each counter has a
-// small fan-in (at most 16 arrivals, 32 for the router and 512 for the
-// shared blocks, whose waits are off the critical path).
+// small fan-in (at most 16 arrivals, 512 for the shared blocks, whose wait is
+// off the critical path).  The router's results need no counter: they travel
+// as tagged words.
 struct Bank {
   uint32_t normc[NQ][16];     // norm slice q: one arrival per row
-  uint32_t router[16];        // router blocks whose logits are final
   uint32_t shared[16];        // shared blocks whose activations are final
   uint32_t routed[NRC][16];   // routed gate/up units done
   uint32_t abort_[16];        // set by a wait that passed its deadline
@@ -508,6 +508,18 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int xzero = p.xzero;
 
   TL(0);
+  // This workgroup's output rows [h0, h0 + hn) of the combine (R hn <= NT: one
+  // element per thread).  Their x and residual are loaded now, so that the
+  // combine at the end does not wait for memory.
+  const int HR = (H + G - 1) / G;
+  const int h0 = cta * HR, hn = max(0, min(H, h0 + HR) - h0);
+  uint32_t cx, cr;
+  {
+    const int r = tid / max(hn, 1), hh = tid - r * max(hn, 1);
+    const uint32_t off = tid < R * hn ? (uint32_t)(r * H + h0 + hh) * 2u : OOB;
+    cx = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.x, (uint32_t)(R * H * 2)), (int)off, 0, 0);
+    cr = p.res ? __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.res, (uint32_t)(R * H * 2)), (int)off, 0, 0) : 0u;
+  }
   // ---- call epoch: every workgroup counts the calls it has started, so all
   // agree on it without a shared ticket (one launch = one call per workgroup).
   // The count is a read-modify-write atomic, like every other control word
@@ -1115,8 +1127,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   TL(8);
 
   // ---- P3: down projections for this workgroup's hidden rows, then combine
-  const int HR = (H + G - 1) / G;
-  const int h0 = cta * HR, hn = max(0, min(H, h0 + HR) - h0);
   const int nblk = (hn + 15) / 16;
   const int CI = I / 32, TI = (CI + 3) / 4;
   const int nsl = D > wave ? (D - wave + NW - 1) / NW : 0;
@@ -1166,36 +1176,22 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   TL(9);
   if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
     return;
-  if (!wait_cnt<true>(p, bk, &bk->routed[0][0], 16, NRC, (uint32_t)(D * (I / 8)), false, &S.flags[4], 3, ep, (uint32_t)D))
-    return;
   if (hn == 0) return;
-  TL(10);
-  {  // stage the routed a [P][I] and the shared a [R][Is] into LDS, plus their zero rows
-    if (tid < P) {  // pick -> its product row: the slot's users in row order
-      const int d = S.eslot[S.ids[tid]], r = tid / K;
-      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
-    }
-    const int nr8 = P * I / 8, ns8 = R * Is / 8, n8 = nr8 + ns8;
-    for (int base = 0; base < n8; base += NT * 4) {
+  {  // stage the shared a [R][Is] into LDS, plus its zero row
+    const int ns8 = R * Is / 8;
+    for (int base = 0; base < ns8; base += NT * 4) {
       u32x4 v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e8 = base + k * NT + tid;
-        v[k] = e8 < nr8 ? ld16<CP_SC1>(rs_ar, (uint32_t)e8 * 16u)
-                        : ld16<CP_SC1>(rs_as, e8 < n8 ? (uint32_t)(e8 - nr8) * 16u : OOB);
+        v[k] = ld16<CP_SC1>(rs_as, e8 < ns8 ? (uint32_t)e8 * 16u : OOB);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e8 = base + k * NT + tid;
-        if (e8 < nr8) {
-          *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
-        } else if (e8 < n8) {
-          const int s8 = e8 - nr8;
-          *(u32x4*)(asl + ((s8 * 8) / Is) * p.ss + (s8 * 8) % Is) = v[k];
-        }
+        if (e8 < ns8) *(u32x4*)(asl + ((e8 * 8) / Is) * p.ss + (e8 * 8) % Is) = v[k];
       }
     }
-    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
     for (int c = tid * 8; c < p.ss; c += NT * 8) *(u32x4*)(asl + szero * p.ss + c) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
   }
@@ -1237,6 +1233,32 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         }
       }
     }
+  }
+  // routed down: it needs every slot's a, so it waits for all gate/up units
+  if (!wait_cnt<true>(p, bk, &bk->routed[0][0], 16, NRC, (uint32_t)(D * (I / 8)), false, &S.flags[4], 3, ep, (uint32_t)D))
+    return;
+  TL(10);
+  {  // stage the routed a [P][I] into LDS, plus its zero row
+    if (tid < P) {  // pick -> its product row: the slot's users in row order
+      const int d = S.eslot[S.ids[tid]], r = tid / K;
+      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
+    }
+    const int nr8 = P * I / 8;
+    for (int base = 0; base < nr8; base += NT * 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        v[k] = ld16<CP_SC1>(rs_ar, e8 < nr8 ? (uint32_t)e8 * 16u : OOB);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        if (e8 < nr8) *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+      }
+    }
+    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
   }
   // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
   {
@@ -1286,14 +1308,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   TL(11);
   __syncthreads();
   // combine in a fixed order: picks in (row, k) order, then the shared part
-  for (int idx = tid; idx < R * hn; idx += NT) {
-    const int r = idx / hn, hh = idx % hn, h = h0 + hh;
+  if (tid < R * hn) {
+    const int r = tid / hn, hh = tid % hn, h = h0 + hh;
     float yr = 0.f;
     for (int k = 0; k < K; ++k) yr += S.w[r * K + k] * s_outp[S.ci[r * K + k] * HR + hh];
     float ys = 0.f;
     if (Is > 0)
       for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
-    const uint32_t hb = f2bf(bf2f(p.x[(size_t)r * H + h]) + (p.res ? bf2f(p.res[(size_t)r * H + h]) : 0.f));
+    const uint32_t hb = f2bf(bf2f(cx) + (p.res ? bf2f(cr) : 0.f));
     p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
     if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
     if (p.dbg_ys) p.dbg_ys[(size_t)r * H + h] = ys;
