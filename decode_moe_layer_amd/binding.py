@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_tail.so")
 OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ETIMEOUT = 0, 1, 2, 3, 4, 5
 SOFTMAX, SIGMOID_BIAS = 0, 1
 DEBUG_STALL = 1
+DEBUG_STALL_ONCE = 2
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EHIP", 5: "ETIMEOUT"}
 
 EXPORTS = ("moe_tail_check_config", "moe_tail_create", "moe_tail_run", "moe_tail_get_error",

@@ -1407,6 +1407,7 @@ struct moe_tail {
   uint16_t* a_s;
   uint16_t* a_r;
   int S1, TC, n_rb, n_sb, Ep;
+  int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
   char err[256];
 };
 
@@ -1438,7 +1439,8 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
   if (c->scoring != MOE_TAIL_SOFTMAX && c->scoring != MOE_TAIL_SIGMOID_BIAS)
     return fail(nullptr, MOE_TAIL_EINVAL, "unknown scoring %d", c->scoring);
   if (!(c->eps > 0.f) || !isfinite(c->eps)) return fail(nullptr, MOE_TAIL_EINVAL, "eps must be positive and finite");
-  if (c->debug_flags & ~MOE_TAIL_DEBUG_STALL) return fail(nullptr, MOE_TAIL_EINVAL, "unknown debug_flags bits");
+  if (c->debug_flags & ~(MOE_TAIL_DEBUG_STALL | MOE_TAIL_DEBUG_STALL_ONCE))
+    return fail(nullptr, MOE_TAIL_EINVAL, "unknown debug_flags bits");
   return MOE_TAIL_OK;
 }
 
@@ -1594,7 +1596,11 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.szero = c.max_rows;
   p.eps = (double)c.eps;
   p.deadline_ticks = h->deadline_ticks;
-  p.debug_flags = c.debug_flags;
+  p.debug_flags = c.debug_flags & MOE_TAIL_DEBUG_STALL;
+  if ((c.debug_flags & MOE_TAIL_DEBUG_STALL_ONCE) && !h->stall_spent) {
+    p.debug_flags |= MOE_TAIL_DEBUG_STALL;
+    h->stall_spent = 1;
+  }
   p.debug_block = c.debug_block;
   p.x = (const uint16_t*)a->x;
   p.res = (const uint16_t*)a->residual;

@@ -56,6 +56,9 @@ typedef enum { MOE_TAIL_SOFTMAX = 0, MOE_TAIL_SIGMOID_BIAS = 1 } moe_tail_scorin
 /* debug_flags bit: the workgroup `debug_block` never proceeds past its first
  * cross-workgroup wait until that wait's deadline fires (fault drill). */
 #define MOE_TAIL_DEBUG_STALL 1u
+/* debug_flags bit: the same, on the handle's first call only; later calls
+ * run normally (drill of the recovery on one handle). */
+#define MOE_TAIL_DEBUG_STALL_ONCE 2u
 
 typedef struct {
   int32_t max_rows;     /* largest `rows` any run will pass: 1..16 */
@@ -68,7 +71,7 @@ typedef struct {
   float eps;            /* RMSNorm epsilon, > 0 */
   int32_t device;       /* HIP device ordinal, or -1 for the current device */
   uint32_t deadline_us; /* per-wait deadline in microseconds; 0 selects 200000 */
-  uint32_t debug_flags; /* 0 in production; see MOE_TAIL_DEBUG_STALL */
+  uint32_t debug_flags; /* 0 in production; see MOE_TAIL_DEBUG_STALL(_ONCE) */
   int32_t debug_block;  /* workgroup index used by debug_flags */
 } moe_tail_config;
 

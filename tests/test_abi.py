@@ -46,13 +46,20 @@ def test_check_config_accepts_the_workloads():
     ("max_rows", 0), ("max_rows", 17), ("hidden", 100), ("hidden", 6000), ("hidden", 32768),
     ("num_experts", 0), ("num_experts", 513), ("top_k", 0), ("top_k", 33), ("inter", 48), ("inter", 0),
     ("shared_inter", 40), ("shared_inter", -32), ("scoring", 2), ("eps", 0.0), ("eps", float("nan")),
-    ("debug_flags", 6),
+    ("debug_flags", 4), ("debug_flags", 6),
 ])
 def test_check_config_refusals(field, value):
     c = good()
     setattr(c, field, value)
     assert binding.check_config(c) == binding.EINVAL
     assert binding.strerror(None)
+
+
+def test_debug_flags_accepted():
+    for flags in (binding.DEBUG_STALL, binding.DEBUG_STALL_ONCE, binding.DEBUG_STALL | binding.DEBUG_STALL_ONCE):
+        c = good()
+        c.debug_flags = flags
+        assert binding.check_config(c) == binding.OK, flags
 
 
 def test_topk_above_experts_refused():

@@ -132,3 +132,24 @@ def test_calls_after_a_timeout_fail_fast_until_the_error_is_read():
     assert bad.get_error() == binding.ETIMEOUT
     msg = binding.strerror(bad.h)
     assert "deadline" in msg and "epochs" in msg, msg
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 1), ("c1", 8)])
+def test_same_handle_is_correct_after_a_timeout(name, rows):
+    """The first call times out (one workgroup held from the host); reading the
+    error resets the handle, whose epochs then start over.  The next calls on
+    the same handle must be correct: no word left by the failed call may pass
+    for one of theirs.  c0 sums the router partials in every workgroup, c1 at 8
+    rows reads the logits of the blocks' last chunks."""
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    dw = device_weights(name)
+    h = handle_for(cfg, deadline_us=20000, debug_flags=binding.DEBUG_STALL_ONCE, debug_block=3)
+    run(h, cfg, dw, x, r)
+    assert h.get_error() == binding.ETIMEOUT
+    for _ in range(2):
+        g = run(h, cfg, dw, x, r)
+        assert h.get_error() == binding.OK
+        check_against_oracle(g, o, cfg)
