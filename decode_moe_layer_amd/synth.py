@@ -38,6 +38,7 @@ import numpy as np
 # stream ids of the seed tree
 _S_GAMMA, _S_ROUTER, _S_BIAS, _S_W13Q, _S_W13S, _S_W2Q, _S_W2S = 1, 2, 3, 4, 5, 6, 7
 _S_WS13, _S_WS2, _S_ROWS, _S_TAIL, _S_BASE = 8, 9, 10, 11, 12
+_S_SGATE = 13
 
 SOFTMAX = 0
 SIGMOID_BIAS = 1
@@ -117,6 +118,13 @@ def make_weights(cfg: Config, experts: Optional[int] = None) -> dict:
         w["ws13"] = None
         w["ws2"] = None
     return w
+
+
+def make_shared_gate(cfg: Config) -> np.ndarray:
+    """Shared-expert gate weights [H] (bf16 bits) ~ bf16(N(0, 1/hidden)), from a
+    stream of their own (the other weights do not change with or without it)."""
+    std = 1.0 / math.sqrt(cfg.hidden)
+    return to_bf16_bits(_rng(cfg, _S_SGATE).standard_normal(cfg.hidden, dtype=np.float32) * std)
 
 
 def make_router_weights(cfg: Config, experts: Optional[int] = None) -> dict:

@@ -59,7 +59,7 @@ def lib():
         L.oracle_norm_row.restype = None
         L.oracle_norm_row.argtypes = [i, d, p, p, p, p, p, p]
         L.oracle_moe_tail.restype = i
-        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d] + [p] * 20
+        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d] + [p] * 21
         L.oracle_router_keys.restype = i
         L.oracle_router_keys.argtypes = [i, i, i, i, d] + [p] * 7
         _lib = L
@@ -147,7 +147,8 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
 
     Returns a dict with h, xn, out ([R, H] bf16 bits), logits, keys ([R, E]
     float64), ids ([R, K] int32), w ([R, K] float64), y_routed, y_shared
-    ([R, H] float64).
+    ([R, H] float64).  w may hold "shared_gate" ([H] bf16 bits): the shared
+    output is then scaled by sigmoid(shared_gate . xn); y_shared is gated.
     """
     R, H = x.shape
     E, K, I, Is = cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter
@@ -160,7 +161,8 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
         R, H, E, K, I, Is, cfg.scoring, float(np.float32(cfg.eps)),
         _ptr(np.ascontiguousarray(x)), _ptr(None if r is None else np.ascontiguousarray(r)), _ptr(w["gamma"]),
         _ptr(w["router_w"]), _ptr(w.get("router_bias")), _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w2_q"]),
-        _ptr(w["w2_s"]), _ptr(w.get("ws13")), _ptr(w.get("ws2")), _ptr(o["h"]), _ptr(o["xn"]), _ptr(o["logits"]),
+        _ptr(w["w2_s"]), _ptr(w.get("ws13")), _ptr(w.get("ws2")), _ptr(w.get("shared_gate")), _ptr(o["h"]),
+        _ptr(o["xn"]), _ptr(o["logits"]),
         _ptr(o["keys"]), _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["y_routed"]), _ptr(o["y_shared"]), _ptr(o["out"]),
     )
     if rc != 0:

@@ -19,6 +19,7 @@
  *   for each pick e in S:  [g | u] = deq(W13[e]) xn,  a = g*sigmoid(g)*u,
  *                          d_e = deq(W2[e]) a
  *   s      = Ws2 (silu(Ws13_gate xn) * Ws13_up xn)   bf16 shared expert
+ *   s      = sigmoid(wg . xn) s        only when a shared gate wg [H] is given
  *   y      = sum_k w_k d_{S_k} + s ;   out = bf16(h + y)
  *
  * Sources (page titles; no listing is followed line by line):
@@ -28,6 +29,9 @@
  *     experts gate/up + SiLU*up + down, bf16 shared expert, residual output).
  *   - "glm53: Long-context indexer ..." (sgl-amd-mono PR 86), PR 85 commit
  *     rows 9 and 20: top-k rounds that resolve exact ties toward the lower id.
+ *   - the same K2 commit text, "Kernel Replacement": the shared expert's
+ *     output is scaled by a sigmoid gate of the normed row
+ *     (_fused_gate_sigmoid_mul_add_kernel); optional here.
  *   - OCP Microscaling Formats (MX) v1.0: E2M1 element and E8M0 scale
  *     encodings, blocks of 32 elements (the pages name MXFP4 but do not
  *     define it).
@@ -210,13 +214,22 @@ void oracle_shared_row(int H, int Is, const uint16_t* xn, const uint16_t* ws13, 
   free(a);
 }
 
+/* The shared expert's gate: sigmoid(wg . xn), the dot product in double. */
+double oracle_shared_gate(int H, const uint16_t* xn, const uint16_t* wg) {
+  double g = 0.0;
+  for (int j = 0; j < H; j++) g += bfd(wg, j) * bfd(xn, j);
+  return sigmoid(g);
+}
+
 /* The whole tail for `rows` rows.  Every output pointer may be NULL except
  * out.  Shapes: x, r, h_out, xn_out, out: [rows, H] bf16 bits; logits, keys:
- * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H]. */
+ * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H].  sgate [H]
+ * may be NULL (no shared gate); y_shared is the gated shared output. */
 int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps,
                     const uint16_t* x, const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w,
                     const float* bias, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                    const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, uint16_t* h_out,
+                    const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, const uint16_t* sgate,
+                    uint16_t* h_out,
                     uint16_t* xn_out, double* logits_out, double* keys_out, int32_t* ids_out, double* w_out,
                     double* y_routed_out, double* y_shared_out, uint16_t* out) {
   if (rows < 0 || H <= 0 || H % 32 || E <= 0 || K <= 0 || K > E || I <= 0 || I % 32 || Is < 0 || !out) return 1;
@@ -247,6 +260,10 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
     }
     for (int j = 0; j < H; j++) ys[j] = 0.0;
     if (Is > 0) oracle_shared_row(H, Is, xn, ws13, ws2, ys);
+    if (Is > 0 && sgate) {
+      const double sg = oracle_shared_gate(H, xn, sgate);
+      for (int j = 0; j < H; j++) ys[j] *= sg;
+    }
     for (int j = 0; j < H; j++) out[ro + j] = oracle_bf16_round(bfd(h, j) + (yr[j] + ys[j]));
     if (h_out) memcpy(h_out + ro, h, sizeof(uint16_t) * (size_t)H);
     if (xn_out) memcpy(xn_out + ro, xn, sizeof(uint16_t) * (size_t)H);

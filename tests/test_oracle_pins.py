@@ -381,3 +381,51 @@ def test_power_of_two_scale_linearity():
     s[:, cfg.inter:, :] += 1
     wu["w13_s"] = s
     np.testing.assert_array_equal(oracle.moe_tail(x, r, wu, cfg)["y_routed"], 2.0 * base)
+
+
+# ---- the shared expert's sigmoid gate (optional; "[AMD] integrate kimi k3
+# monokernel", K2 commit text, "Kernel Replacement") ---------------------------
+
+def _gated(cfg, w, x, r, gate_f32):
+    wg = dict(w)
+    wg["shared_gate"] = synth.to_bf16_bits(np.asarray(gate_f32, np.float32))
+    return oracle.moe_tail(x, r, wg, cfg)
+
+
+def test_shared_gate_closed_forms():
+    """sigmoid(0) = 1/2 halves the shared output exactly; a gate whose dot
+    product with xn is about +-200 saturates to exactly 1 (unchanged) or to
+    below 1e-80 (gone); the routed part and the routing never change."""
+    cfg = synth.CONFIGS["c0"].with_rows(2)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    o = oracle.moe_tail(x, r, w, cfg)
+    H = cfg.hidden
+    half = _gated(cfg, w, x, r, np.zeros(H))
+    np.testing.assert_array_equal(half["y_shared"], 0.5 * o["y_shared"])
+    np.testing.assert_array_equal(half["y_routed"], o["y_routed"])
+    np.testing.assert_array_equal(half["ids"], o["ids"])
+    for row in range(cfg.rows):
+        sgn = np.sign(synth.bf16_bits_to_f32(o["xn"][row]))
+        on = _gated(cfg, w, x[row:row + 1], r[row:row + 1], 0.5 * sgn)
+        off = _gated(cfg, w, x[row:row + 1], r[row:row + 1], -0.5 * sgn)
+        np.testing.assert_array_equal(on["y_shared"][0], o["y_shared"][row])
+        assert np.max(np.abs(off["y_shared"][0])) <= 1e-80 * np.max(np.abs(o["y_shared"][row]))
+
+
+def test_shared_gate_reads_the_normed_row():
+    """A one-hot gate e_k picks channel k of xn (not of h or x): the shared
+    output is scaled by sigmoid(xn_k), for a few channels k."""
+    cfg = synth.CONFIGS["c0"].with_rows(1)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    o = oracle.moe_tail(x, r, w, cfg)
+    xn = synth.bf16_bits_to_f32(o["xn"][0]).astype(np.float64)
+    h = synth.bf16_bits_to_f32(o["h"][0]).astype(np.float64)
+    for k in (0, 7, 255, 511):
+        assert xn[k] != h[k]
+        e = np.zeros(cfg.hidden)
+        e[k] = 1.0
+        g = _gated(cfg, w, x, r, e)
+        ratio = g["y_shared"][0] / o["y_shared"][0]
+        np.testing.assert_allclose(ratio, 1.0 / (1.0 + np.exp(-xn[k])), rtol=1e-13)
