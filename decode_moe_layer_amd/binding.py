@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
 class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "residual", "gamma", "router_w", "router_bias", "w13_q", "w13_s", "w2_q", "w2_s", "ws13", "ws2",
-        "out", "res_out", "topk_ids", "topk_w", "dbg_logits", "dbg_y_routed", "dbg_y_shared")]
+        "out", "res_out", "topk_ids", "topk_w", "dbg_logits", "dbg_y_routed", "dbg_y_shared", "shared_gate")]
 
 
 class MoeTailError(RuntimeError):
@@ -105,10 +105,11 @@ class MoeTail:
 
     def run(self, rows, x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13, ws2, out,
             res_out=None, topk_ids=None, topk_w=None, dbg_logits=None, dbg_y_routed=None, dbg_y_shared=None,
-            stream=None):
+            stream=None, shared_gate=None):
         """Enqueue one call; tensors are torch device tensors (or raw device addresses)."""
         a = Args(*[_ptr(t) for t in (x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13,
-                                     ws2, out, res_out, topk_ids, topk_w, dbg_logits, dbg_y_routed, dbg_y_shared)])
+                                     ws2, out, res_out, topk_ids, topk_w, dbg_logits, dbg_y_routed, dbg_y_shared,
+                                     shared_gate)])
         if stream is None:
             import torch
 

@@ -121,6 +121,7 @@ struct Params {
   const uint8_t* w2s;
   const uint16_t* ws13;
   const uint16_t* ws2;
+  const uint16_t* sgate;  // [H] shared-expert gate, or null
   uint16_t* out;
   uint16_t* res_out;
   int32_t* topk_ids;
@@ -133,6 +134,7 @@ struct Params {
   uint64_t* xnt;    // [R][H/2] tagged xn pairs (this call's K-chunk readers)
   uint64_t* lgt;    // [R][Ep] tagged fp32 logits
   uint64_t* part1;  // [blocks * S1][16][16] tagged fp32 K-chunk partial sums
+  uint64_t* gpart;  // [R][NQ] tagged fp32 partial dots of the shared gate, one per norm slice
   uint16_t* a_s;
   uint16_t* a_r;
 };
@@ -468,6 +470,9 @@ struct Shared {
   uint32_t flags[8];
   uint32_t ep;
   double tmpd[NW];
+  float tmpg[NW];             // shared gate: each wave's partial dot of a norm slice
+  float gsum[MAX_R * NQ];     // shared gate: the slices' partial dots, per row
+  float sgw[MAX_R];           // shared gate: sigmoid(wg . xn) per row
   int wcnt[NW];
   int ucnt[NW];
   int last[MAX_ITEMS1];
@@ -594,6 +599,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     const u32x4 x8 = ld16<0>(rx, sl ? (uint32_t)i * 2u : OOB);
     const u32x4 r8 = ld16<0>(rr, sl ? (uint32_t)i * 2u : OOB);
     const u32x4 g8 = ld16<0>(rg, sl ? (uint32_t)i * 2u : OOB);
+    u32x4 wg8 = {0u, 0u, 0u, 0u};  // shared gate slice
+    if (p.sgate) wg8 = ld16<0>(make_rsrc(p.sgate, (uint32_t)(H * 2)), sl ? (uint32_t)i * 2u : OOB);
     double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -613,6 +620,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     double tot = 0.0;
     for (int w = 0; w < NW; ++w) tot += S.tmpd[w];
     const double rstd = 1.0 / sqrt(tot / (double)H + p.eps);
+    u32x4 nvs = {0u, 0u, 0u, 0u};  // this thread's 8 xn values (zeros outside the slice)
     if (sl) {
       u32x4 hv, nv;
 #pragma unroll
@@ -628,6 +636,25 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) st_tag(p.xnt + (size_t)(row * H + i) / 2 + c, nv[c], epn);
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
+      nvs = nv;
+    }
+    if (p.sgate) {  // this slice's share of the gate's dot product: lanes, waves in order
+      float gd = 0.f;
+      if (sl) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          gd += bf2f(nvs[c] & 0xFFFFu) * bf2f(wg8[c] & 0xFFFFu);
+          gd += bf2f(nvs[c] >> 16) * bf2f(wg8[c] >> 16);
+        }
+      }
+      gd = wave_sum_f32(gd);
+      if (lane == 0) S.tmpg[wave] = gd;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < NW; ++w) t += S.tmpg[w];
+        st_tag(p.gpart + row * NQ + q, __float_as_uint(t), epn);
+      }
     }
   }
   if (tid == 0) {
@@ -1171,6 +1198,26 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     return f;
   };
+  // the shared gate of every row: the norm slices' partial dots, long written
+  // by now, summed in slice order (before the down weights' loads go out)
+  if (p.sgate && Is > 0 && hn > 0) {
+    if (!poll_all([&]() {
+          bool ok = true;
+          if (tid < R * NQ) {
+            const uint64_t w = ld_tag(p.gpart + tid);
+            ok = tag_ok(w, ep);
+            S.gsum[tid] = __uint_as_float((uint32_t)w);
+          }
+          return ok;
+        }, 2, 1, false))
+      return;
+    if (tid < R) {
+      float t = 0.f;
+      for (int q = 0; q < NQ; ++q) t += S.gsum[tid * NQ + q];
+      S.sgw[tid] = 1.f / (1.f + __expf(-t));
+    }
+    __syncthreads();
+  }
   Window<2, FragD> w3;
   w3.prime(p3_next);
   TL(9);
@@ -1315,6 +1362,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     float ys = 0.f;
     if (Is > 0)
       for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
+    if (p.sgate && Is > 0) ys *= S.sgw[r];
     const uint32_t hb = f2bf(bf2f(cx) + (p.res ? bf2f(cr) : 0.f));
     p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
     if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
@@ -1403,6 +1451,7 @@ struct moe_tail {
   uint64_t* xnt;
   uint64_t* lgt;
   uint64_t* part1;
+  uint64_t* gpart;
   size_t scratch_bytes;
   uint16_t* a_s;
   uint16_t* a_r;
@@ -1501,7 +1550,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_xnt = o_xn + al(R * H * 2);
   const size_t o_lg = o_xnt + al(R * H * 4), o_pt = o_lg + al(R * (size_t)h->Ep * 8);
-  const size_t o_as = o_pt + al((size_t)n_it * 2048);
+  const size_t o_gp = o_pt + al((size_t)n_it * 2048), o_as = o_gp + al(R * mt::NQ * 8);
   const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
   (void)E;
   int prev = 0;
@@ -1533,6 +1582,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->xnt = (uint64_t*)(base + o_xnt);
   h->lgt = (uint64_t*)(base + o_lg);
   h->part1 = (uint64_t*)(base + o_pt);
+  h->gpart = (uint64_t*)(base + o_gp);
   h->scratch_bytes = total;
   h->a_s = (uint16_t*)(base + o_as);
   h->a_r = (uint16_t*)(base + o_ar);
@@ -1556,6 +1606,8 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   }
   if (a->residual && !aligned(a->residual, 16)) return fail(h, MOE_TAIL_EINVAL, "residual is not 16-byte aligned");
   if (a->res_out && !aligned(a->res_out, 16)) return fail(h, MOE_TAIL_EINVAL, "res_out is not 16-byte aligned");
+  if (a->shared_gate && !aligned(a->shared_gate, 16))
+    return fail(h, MOE_TAIL_EINVAL, "shared_gate is not 16-byte aligned");
   if (c.scoring == MOE_TAIL_SIGMOID_BIAS && (!a->router_bias || !aligned(a->router_bias, 4)))
     return fail(h, MOE_TAIL_EINVAL, "router_bias is required (4-byte aligned) for sigmoid scoring");
   if (c.shared_inter > 0) {
@@ -1613,6 +1665,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.w2s = a->w2_s;
   p.ws13 = (const uint16_t*)a->ws13;
   p.ws2 = (const uint16_t*)a->ws2;
+  p.sgate = (const uint16_t*)a->shared_gate;
   p.out = (uint16_t*)a->out;
   p.res_out = (uint16_t*)a->res_out;
   p.topk_ids = a->topk_ids;
@@ -1625,6 +1678,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.xnt = h->xnt;
   p.lgt = h->lgt;
   p.part1 = h->part1;
+  p.gpart = h->gpart;
   p.a_s = h->a_s;
   p.a_r = h->a_r;
 

@@ -95,7 +95,12 @@ typedef struct {
   float* topk_w;            /* [rows, K] normalised weights, or NULL */
   float* dbg_logits;        /* [rows, E] router logits, or NULL */
   float* dbg_y_routed;      /* [rows, H] fp32 routed sum, or NULL */
-  float* dbg_y_shared;      /* [rows, H] fp32 shared expert output, or NULL */
+  float* dbg_y_shared;      /* [rows, H] fp32 shared expert output (after its gate), or NULL */
+  /* optional input, after the outputs so that earlier callers' layouts hold */
+  const void* shared_gate;  /* [H] bf16 gate wg, 16-byte aligned, or NULL: the shared output is
+                               scaled by sigmoid(wg . xn) per row ("[AMD] integrate kimi k3
+                               monokernel", K2 commit text, Kernel Replacement: the fused
+                               gate-sigmoid-mul-add on the shared expert); ignored when Is == 0 */
 } moe_tail_args;
 
 /* Validate a configuration on the host only (no GPU call).  Returns

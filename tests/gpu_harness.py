@@ -53,7 +53,8 @@ def run(handle, cfg, dw, x, r, rows=None, stream=None, debug=True):
         o["y_shared"] = t.empty((R, H), dtype=t.float32, device="cuda")
     handle.run(R, xd, rd, dw["gamma"], dw["router_w"], dw.get("router_bias"), dw["w13_q"], dw["w13_s"], dw["w2_q"],
                dw["w2_s"], dw.get("ws13"), dw.get("ws2"), o["out"], o["res_out"], o["ids"], o["w"],
-               o.get("logits"), o.get("y_routed"), o.get("y_shared"), stream=stream)
+               o.get("logits"), o.get("y_routed"), o.get("y_shared"), stream=stream,
+               shared_gate=dw.get("shared_gate"))
     t.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in o.items()}
     res["out"] = res["out"].view(np.uint16)

@@ -26,9 +26,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # moe_tail_config: 11 x 4-byte fields + float; moe_tail_args: 18 pointers
+    # moe_tail_config: 11 x 4-byte fields + float; moe_tail_args: 19 pointers
     assert ctypes.sizeof(binding.Config) == 12 * 4
-    assert ctypes.sizeof(binding.Args) == 18 * 8
+    assert ctypes.sizeof(binding.Args) == 19 * 8
 
 
 def good():

@@ -60,3 +60,27 @@ def test_no_residual_means_h_is_x():
     g = run(h, cfg, device_weights("c0"), x2, None)
     np.testing.assert_array_equal(g["res_out"], x2)
     check_against_oracle(g, o, cfg)
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 1), ("c1", 8), ("c4", 16)])
+def test_parity_with_a_shared_gate(name, rows):
+    """The shared expert's output scaled by sigmoid(wg . xn) per row ("[AMD]
+    integrate kimi k3 monokernel", K2 commit text, Kernel Replacement), on the
+    three kernel paths: routed sums by every reader (c0), xn in LDS (c1 at 8
+    rows), xn read from global scratch (c4 at 16 rows)."""
+    from gpu_harness import dev
+
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    _say("gate", name, rows)
+    w = dict(weights(name))
+    w["shared_gate"] = synth.make_shared_gate(cfg)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    dw = dict(device_weights(name))
+    dw["shared_gate"] = dev(w["shared_gate"])
+    h = handle_for(cfg)
+    g = run(h, cfg, dw, x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    plain = oracle.moe_tail(x, r, weights(name), cfg)
+    assert not np.allclose(plain["y_shared"], o["y_shared"])  # the gate changed the shared part
