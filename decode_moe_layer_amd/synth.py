@@ -60,6 +60,9 @@ class Config:
     heavy_frac: float = 0.0
     heavy_scale: float = 1.0
     similar: bool = False  # rows share a common Gaussian component (rho)
+    n_group: int = 1  # group-limited routing: expert groups (1: none)
+    topk_group: int = 1  # groups kept
+    routed_scale: float = 1.0  # routed scaling factor on the top-k weights
     seed: int = 0
 
     def with_rows(self, rows: int) -> "Config":

@@ -14,8 +14,11 @@
  *          = sigmoid(l[e]) + b[e]  (sigmoid scoring with a selection bias)
  *   S      = the K experts with the largest keys, ties to the lower id,
  *            listed by (key descending, id ascending)
+ *            (group-limited: only experts of the topk_group groups whose two
+ *            largest keys sum highest; see oracle_topk_grouped)
  *   w      = softmax(l[S])     (softmax scoring; equals p[S]/sum p[S])
  *          = sigmoid(l[S]) / sum sigmoid(l[S])   (sigmoid scoring)
+ *            times the routed scaling factor (1 unless given)
  *   for each pick e in S:  [g | u] = deq(W13[e]) xn,  a = g*sigmoid(g)*u,
  *                          d_e = deq(W2[e]) a
  *   s      = Ws2 (silu(Ws13_gate xn) * Ws13_up xn)   bf16 shared expert
@@ -151,6 +154,51 @@ void oracle_topk(int E, int K, const double* keys, int32_t* ids) {
 }
 
 /* Normalised top-K weights. */
+/* Group-limited top-K: the E experts form n_group groups of E / n_group
+ * consecutive ids.  A group's score is the sum of its two largest keys (its
+ * one key when a group has a single expert).  The topk_group groups with the
+ * largest scores are kept (equal scores: the lower group first), and the
+ * top-K of the kept experts follows, as oracle_topk orders it.  n_group <= 1
+ * is oracle_topk itself.  K must not exceed topk_group * E / n_group. */
+void oracle_topk_grouped(int E, int K, const double* keys, int n_group, int topk_group, int32_t* ids) {
+  if (n_group <= 1) {
+    oracle_topk(E, K, keys, ids);
+    return;
+  }
+  const int gs = E / n_group;
+  double* score = (double*)malloc(sizeof(double) * (size_t)n_group);
+  char* kept = (char*)calloc((size_t)n_group, 1);
+  char* taken = (char*)calloc((size_t)E, 1);
+  for (int g = 0; g < n_group; g++) {
+    double m1 = -INFINITY, m2 = -INFINITY;
+    for (int e = g * gs; e < (g + 1) * gs; e++) {
+      if (keys[e] > m1) {
+        m2 = m1;
+        m1 = keys[e];
+      } else if (keys[e] > m2) {
+        m2 = keys[e];
+      }
+    }
+    score[g] = gs >= 2 ? m1 + m2 : m1;
+  }
+  for (int t = 0; t < topk_group; t++) {
+    int best = -1;
+    for (int g = 0; g < n_group; g++)
+      if (!kept[g] && (best < 0 || score[g] > score[best])) best = g;
+    kept[best] = 1;
+  }
+  for (int k = 0; k < K; k++) {
+    int best = -1;
+    for (int e = 0; e < E; e++)
+      if (kept[e / gs] && !taken[e] && (best < 0 || beats(keys, e, best))) best = e;
+    ids[k] = best;
+    taken[best] = 1;
+  }
+  free(score);
+  free(kept);
+  free(taken);
+}
+
 void oracle_topk_weights(int K, int scoring, const double* logits, const int32_t* ids, double* w) {
   double sum = 0.0;
   if (scoring == 0) {
@@ -225,7 +273,8 @@ double oracle_shared_gate(int H, const uint16_t* xn, const uint16_t* wg) {
  * out.  Shapes: x, r, h_out, xn_out, out: [rows, H] bf16 bits; logits, keys:
  * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H].  sgate [H]
  * may be NULL (no shared gate); y_shared is the gated shared output. */
-int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps,
+int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps, int n_group,
+                    int topk_group, double routed_scale,
                     const uint16_t* x, const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w,
                     const float* bias, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                     const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, const uint16_t* sgate,
@@ -234,6 +283,8 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
                     double* y_routed_out, double* y_shared_out, uint16_t* out) {
   if (rows < 0 || H <= 0 || H % 32 || E <= 0 || K <= 0 || K > E || I <= 0 || I % 32 || Is < 0 || !out) return 1;
   if (scoring == 1 && !bias) return 1;
+  if (n_group > 1 && (E % n_group || topk_group < 1 || topk_group > n_group || K > topk_group * (E / n_group)))
+    return 1;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   double* lg = (double*)malloc(sizeof(double) * (size_t)E);
@@ -250,8 +301,9 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
     oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
     oracle_router_row(H, E, xn, router_w, lg);
     oracle_keys(E, scoring, lg, bias, ky);
-    oracle_topk(E, K, ky, ids);
+    oracle_topk_grouped(E, K, ky, n_group, topk_group, ids);
     oracle_topk_weights(K, scoring, lg, ids, w);
+    for (int k = 0; k < K; k++) w[k] *= routed_scale;
     for (int j = 0; j < H; j++) yr[j] = 0.0;
     for (int k = 0; k < K; k++) {
       const int e = ids[k];

@@ -429,3 +429,71 @@ def test_shared_gate_reads_the_normed_row():
         g = _gated(cfg, w, x, r, e)
         ratio = g["y_shared"][0] / o["y_shared"][0]
         np.testing.assert_allclose(ratio, 1.0 / (1.0 + np.exp(-xn[k])), rtol=1e-13)
+
+
+# ---- routing variants: group-limited top-k and a routed scaling factor -----
+
+def test_grouped_topk_reduces_to_plain_topk():
+    """One group, or every group kept, is the plain top-k (pinned above)."""
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        keys = rng.standard_normal(64)
+        for k in (1, 3, 8):
+            plain = oracle.topk(keys, k)
+            np.testing.assert_array_equal(oracle.topk_grouped(keys, k, 1, 1), plain)
+            np.testing.assert_array_equal(oracle.topk_grouped(keys, k, 8, 8), plain)
+
+
+def test_grouped_topk_worked_example():
+    """16 experts in 4 groups of 4, keep 2 groups, pick 3.  Group scores (two
+    largest keys): g0 0.9+0.1 = 1.0, g1 0.5+0.45 = 0.95, g2 0.8+0 = 0.8, g3 0.6.
+    Kept: g0, g1.  Picks: e0 (0.9), e4 (0.5), e5 (0.45); the plain top-3 would
+    take e8 (0.8) from g2 instead."""
+    keys = np.array([0.9, 0.1, 0.0, 0.0, 0.5, 0.45, 0.0, 0.0, 0.8, 0.0, 0.0, 0.0, 0.3, 0.3, 0.3, 0.3])
+    np.testing.assert_array_equal(oracle.topk_grouped(keys, 3, 4, 2), [0, 4, 5])
+    np.testing.assert_array_equal(oracle.topk(keys, 3), [0, 8, 4])
+
+
+def test_grouped_topk_group_ties_go_to_the_lower_group():
+    """Groups 1 and 2 score alike (0.5 + 0.25 each); with group 0 first, group 1 is kept."""
+    keys = np.array([1.0, 1.0, 0.5, 0.25, 0.5, 0.25, 0.0, 0.0])
+    np.testing.assert_array_equal(oracle.topk_grouped(keys, 3, 4, 2), [0, 1, 2])
+    keys2 = keys.copy()
+    keys2[[2, 3]] = keys[[4, 5]] - np.array([0.0, 1e-9])  # group 1 now a little lower
+    np.testing.assert_array_equal(oracle.topk_grouped(keys2, 3, 4, 2), [0, 1, 4])
+
+
+def test_routed_scale_two_doubles_the_routed_part_exactly():
+    import dataclasses
+
+    cfg = synth.CONFIGS["c0"].with_rows(2)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    o = oracle.moe_tail(x, r, w, cfg)
+    o2 = oracle.moe_tail(x, r, w, dataclasses.replace(cfg, routed_scale=2.0))
+    np.testing.assert_array_equal(o2["ids"], o["ids"])
+    np.testing.assert_array_equal(o2["w"], 2.0 * o["w"])
+    np.testing.assert_array_equal(o2["y_routed"], 2.0 * o["y_routed"])
+    np.testing.assert_array_equal(o2["y_shared"], o["y_shared"])
+
+
+def test_grouped_routing_in_the_tail_keeps_picks_inside_the_kept_groups():
+    """The whole tail with 4 groups of 4 kept out of 16 experts: every pick's
+    group is among the 2 best-scoring groups of its row, and n_group = 1 gives
+    the ungrouped tail exactly."""
+    import dataclasses
+
+    cfg = synth.CONFIGS["c0"].with_rows(3)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    g = dataclasses.replace(cfg, n_group=4, topk_group=2)
+    og = oracle.moe_tail(x, r, w, g)
+    o1 = oracle.moe_tail(x, r, w, dataclasses.replace(cfg, n_group=1, topk_group=1))
+    o = oracle.moe_tail(x, r, w, cfg)
+    np.testing.assert_array_equal(o1["ids"], o["ids"])
+    np.testing.assert_array_equal(o1["out"], o["out"])
+    for row in range(cfg.rows):
+        ky = og["keys"][row].reshape(4, 4)
+        top2 = -np.sort(-ky, axis=1)[:, :2].sum(axis=1)
+        kept = set(np.argsort(-top2, kind="stable")[:2].tolist())
+        assert {int(e) // 4 for e in og["ids"][row]} <= kept
