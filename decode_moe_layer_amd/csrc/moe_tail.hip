@@ -97,6 +97,8 @@ struct Ctl {
 
 struct Params {
   int R, H, E, K, I, Is, scoring, G;
+  int n_group, topk_group;  // group-limited routing (n_group 1: none)
+  float rscale;             // routed scaling factor
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
   int rsum;                       // top-k readers sum the router K-chunk partials themselves
   int xs, as, ss;                 // LDS row strides (bf16 elements): xn, routed a, shared a
@@ -232,6 +234,11 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// the float a key came from (finite floats only)
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // Wave-wide reductions to lane 63 with DPP row shifts and row broadcasts,
@@ -493,7 +500,7 @@ constexpr int RED_FLOATS = 2 * NW * 64 * 4;  // floats in Shared::red
 
 // ------------------------------------------------------------------ kernel --
 
-template <bool XL, bool RS>
+template <bool XL, bool RS, bool FEAT>
 __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int tid = threadIdx.x, lane = tid & 63, cta = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -600,7 +607,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     const u32x4 r8 = ld16<0>(rr, sl ? (uint32_t)i * 2u : OOB);
     const u32x4 g8 = ld16<0>(rg, sl ? (uint32_t)i * 2u : OOB);
     u32x4 wg8 = {0u, 0u, 0u, 0u};  // shared gate slice
-    if (p.sgate) wg8 = ld16<0>(make_rsrc(p.sgate, (uint32_t)(H * 2)), sl ? (uint32_t)i * 2u : OOB);
+    if (FEAT && p.sgate) wg8 = ld16<0>(make_rsrc(p.sgate, (uint32_t)(H * 2)), sl ? (uint32_t)i * 2u : OOB);
     double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -638,7 +645,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
       nvs = nv;
     }
-    if (p.sgate) {  // this slice's share of the gate's dot product: lanes, waves in order
+    if (FEAT && p.sgate) {  // this slice's share of the gate's dot product: lanes, waves in order
       float gd = 0.f;
       if (sl) {
 #pragma unroll
@@ -925,6 +932,35 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     MT_CX(2, 4) MT_CX(3, 5)
     MT_CX(1, 2) MT_CX(3, 4) MT_CX(5, 6)
 #undef MT_CX
+    if (FEAT && p.n_group > 1) {
+      // group-limited routing: lanes hold 8 consecutive experts, so a group is
+      // gl aligned lanes.  Their two largest keys merge by a butterfly (every
+      // lane of the group ends with the group's pair), the groups are ranked
+      // by the pair's sum in topk_group rounds (equal sums: the lowest lane,
+      // i.e. the lower group), and the experts of the other groups drop out.
+      const int gl = E / p.n_group / 8;
+      float a1 = key_float((uint32_t)(qv[0] >> 32)), a2 = key_float((uint32_t)(qv[1] >> 32));
+      for (int off = 1; off < gl; off <<= 1) {
+        const float b1 = __shfl_xor(a1, off), b2 = __shfl_xor(a2, off);
+        const float n2 = a1 >= b1 ? fmaxf(b1, a2) : fmaxf(a1, b2);
+        a1 = fmaxf(a1, b1);
+        a2 = n2;
+      }
+      uint32_t gk = e0 < E ? ord_key(a1 + a2) : 0u;
+      bool kept = false;
+      for (int t = 0; t < p.topk_group; ++t) {
+        const uint32_t m = wave_max_u32(gk);
+        const int wl = __ffsll((unsigned long long)__ballot(gk == m)) - 1;
+        if (lane / gl == wl / gl) {
+          kept = true;
+          gk = 0u;
+        }
+      }
+      if (!kept) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[j] = 0;
+      }
+    }
     int myid = 0;
     for (int k = 0; k < K; ++k) {
       const uint32_t head = (uint32_t)(qv[0] >> 32);
@@ -952,7 +988,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     const float sum = wave_sum_f32(t);
     if (lane < K) {
       S.ids[r * K + lane] = (int16_t)myid;
-      S.w[r * K + lane] = t / sum;
+      S.w[r * K + lane] = t / sum * p.rscale;
       atomicOr(&S.rowmask[myid], 1u << r);
     }
   }
@@ -1200,7 +1236,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   };
   // the shared gate of every row: the norm slices' partial dots, long written
   // by now, summed in slice order (before the down weights' loads go out)
-  if (p.sgate && Is > 0 && hn > 0) {
+  if (FEAT && p.sgate && Is > 0 && hn > 0) {
     if (!poll_all([&]() {
           bool ok = true;
           if (tid < R * NQ) {
@@ -1362,7 +1398,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     float ys = 0.f;
     if (Is > 0)
       for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
-    if (p.sgate && Is > 0) ys *= S.sgw[r];
+    if (FEAT && p.sgate && Is > 0) ys *= S.sgw[r];
     const uint32_t hb = f2bf(bf2f(cx) + (p.res ? bf2f(cr) : 0.f));
     p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
     if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
@@ -1373,25 +1409,28 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 
 // Separate kernels rather than run-time branches, so that each launch's code
 // is compact: activations staged in LDS, or read from global scratch (wide
-// rows); router sums by the last chunk's workgroup, or by every reader.
-__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_lds(Params p) {
-  __shared__ Shared S;
-  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
-  tail<true, false>(p, S, s_dyn);
-}
-__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_lds_rs(Params p) {
-  __shared__ Shared S;
-  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
-  tail<true, true>(p, S, s_dyn);
-}
-__global__ __launch_bounds__(NT, 1) void moe_tail_kernel_gm(Params p) {
-  __shared__ Shared S;
-  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
-  tail<false, false>(p, S, s_dyn);
-}
+// rows); router sums by the last chunk's workgroup, or by every reader.  The
+// _f kernels add the optional steps (the shared expert's gate, group-limited
+// routing).  A call runs its code once, front to back, so code it does not
+// execute still costs instruction fetches: the plain kernels carry none of it.
+#define MT_KERNEL(NAME, XL, RS, FEAT)                            \
+  __global__ __launch_bounds__(NT, 1) void NAME(Params p) {      \
+    __shared__ Shared S;                                         \
+    extern __shared__ __attribute__((aligned(16))) char s_dyn[]; \
+    tail<XL, RS, FEAT>(p, S, s_dyn);                             \
+  }
+MT_KERNEL(moe_tail_kernel_lds, true, false, false)
+MT_KERNEL(moe_tail_kernel_lds_rs, true, true, false)
+MT_KERNEL(moe_tail_kernel_gm, false, false, false)
+MT_KERNEL(moe_tail_kernel_lds_f, true, false, true)
+MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true)
+MT_KERNEL(moe_tail_kernel_gm_f, false, false, true)
+#undef MT_KERNEL
 static const void* kernel_for(const Params& p) {
-  if (!p.xn_lds) return (const void*)moe_tail_kernel_gm;
-  return p.rsum ? (const void*)moe_tail_kernel_lds_rs : (const void*)moe_tail_kernel_lds;
+  const bool f = p.sgate || p.n_group > 1;
+  if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f : (const void*)moe_tail_kernel_gm;
+  if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f : (const void*)moe_tail_kernel_lds_rs;
+  return f ? (const void*)moe_tail_kernel_lds_f : (const void*)moe_tail_kernel_lds;
 }
 
 }  // namespace mt
@@ -1488,6 +1527,15 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
   if (c->scoring != MOE_TAIL_SOFTMAX && c->scoring != MOE_TAIL_SIGMOID_BIAS)
     return fail(nullptr, MOE_TAIL_EINVAL, "unknown scoring %d", c->scoring);
   if (!(c->eps > 0.f) || !isfinite(c->eps)) return fail(nullptr, MOE_TAIL_EINVAL, "eps must be positive and finite");
+  if (c->n_group < 0 || (c->n_group > 1 && (c->num_experts % c->n_group || (c->num_experts / c->n_group) % 8)))
+    return fail(nullptr, MOE_TAIL_EINVAL, "n_group %d must divide num_experts %d into groups of a multiple of 8",
+                c->n_group, c->num_experts);
+  if (c->n_group > 1 && (c->topk_group < 1 || c->topk_group > c->n_group ||
+                         c->top_k > c->topk_group * (c->num_experts / c->n_group)))
+    return fail(nullptr, MOE_TAIL_EINVAL, "topk_group %d must be in 1..n_group and keep at least top_k experts",
+                c->topk_group);
+  if (!(c->routed_scale >= 0.f) || !isfinite(c->routed_scale))
+    return fail(nullptr, MOE_TAIL_EINVAL, "routed_scale must be finite and not negative");
   if (c->debug_flags & ~(MOE_TAIL_DEBUG_STALL | MOE_TAIL_DEBUG_STALL_ONCE))
     return fail(nullptr, MOE_TAIL_EINVAL, "unknown debug_flags bits");
   return MOE_TAIL_OK;
@@ -1563,12 +1611,13 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
     return fail(nullptr, MOE_TAIL_ENOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
   }
   e = hipMemset(h->scratch, 0, total);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(plan.xn_lds ? (const void*)mt::moe_tail_kernel_lds : (const void*)mt::moe_tail_kernel_gm,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-  if (e == hipSuccess && plan.xn_lds)
-    e = hipFuncSetAttribute((const void*)mt::moe_tail_kernel_lds_rs, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)dyn);
+  {
+    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds, (const void*)mt::moe_tail_kernel_lds_rs,
+                        (const void*)mt::moe_tail_kernel_lds_f, (const void*)mt::moe_tail_kernel_lds_rs_f,
+                        (const void*)mt::moe_tail_kernel_gm, (const void*)mt::moe_tail_kernel_gm_f};
+    for (int k = plan.xn_lds ? 0 : 4; k < (plan.xn_lds ? 4 : 6) && e == hipSuccess; ++k)
+      e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) {
@@ -1627,6 +1676,9 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.I = c.inter;
   p.Is = c.shared_inter;
   p.scoring = c.scoring;
+  p.n_group = c.n_group > 1 ? c.n_group : 1;
+  p.topk_group = c.n_group > 1 ? c.topk_group : 1;
+  p.rscale = c.routed_scale > 0.f ? c.routed_scale : 1.f;
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
   // reader-side router sums when each thread then loads at most 8 partials

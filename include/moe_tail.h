@@ -73,6 +73,14 @@ typedef struct {
   uint32_t deadline_us; /* per-wait deadline in microseconds; 0 selects 200000 */
   uint32_t debug_flags; /* 0 in production; see MOE_TAIL_DEBUG_STALL(_ONCE) */
   int32_t debug_block;  /* workgroup index used by debug_flags */
+  /* routing variants, after the earlier fields so that zeroed configs keep
+   * the plain routing: */
+  int32_t n_group;      /* group-limited routing: groups of E / n_group consecutive experts (a multiple
+                           of 8); a group scores the sum of its two largest selection keys, the
+                           topk_group best groups are kept (equal scores: the lower group) and the
+                           top-k is taken among their experts.  0 or 1: no groups */
+  int32_t topk_group;   /* groups kept, 1..n_group, with K <= topk_group * E / n_group */
+  float routed_scale;   /* routed scaling factor on the top-k weights; 0 means 1 */
 } moe_tail_config;
 
 typedef struct {

@@ -26,8 +26,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # moe_tail_config: 11 x 4-byte fields + float; moe_tail_args: 19 pointers
-    assert ctypes.sizeof(binding.Config) == 12 * 4
+    # moe_tail_config: 13 x 4-byte integer fields + 2 floats; moe_tail_args: 19 pointers
+    assert ctypes.sizeof(binding.Config) == 15 * 4
     assert ctypes.sizeof(binding.Args) == 19 * 8
 
 
@@ -47,12 +47,30 @@ def test_check_config_accepts_the_workloads():
     ("num_experts", 0), ("num_experts", 513), ("top_k", 0), ("top_k", 33), ("inter", 48), ("inter", 0),
     ("shared_inter", 40), ("shared_inter", -32), ("scoring", 2), ("eps", 0.0), ("eps", float("nan")),
     ("debug_flags", 4), ("debug_flags", 6),
+    ("n_group", 3), ("n_group", 128), ("n_group", -1),
+    ("routed_scale", -1.0), ("routed_scale", float("inf")),
 ])
 def test_check_config_refusals(field, value):
     c = good()
     setattr(c, field, value)
     assert binding.check_config(c) == binding.EINVAL
     assert binding.strerror(None)
+
+
+def test_grouped_routing_accepted_and_refused():
+    c = good()  # 512 experts, top-10
+    c.n_group, c.topk_group, c.routed_scale = 8, 4, 2.5
+    assert binding.check_config(c) == binding.OK
+    c.topk_group = 1  # 64 experts kept >= 10 picks
+    assert binding.check_config(c) == binding.OK
+    c.n_group, c.topk_group = 64, 1  # 8 experts kept < 10 picks
+    assert binding.check_config(c) == binding.EINVAL
+    c.n_group, c.topk_group = 8, 0
+    assert binding.check_config(c) == binding.EINVAL
+    c.topk_group = 9
+    assert binding.check_config(c) == binding.EINVAL
+    c.n_group, c.topk_group, c.routed_scale = 0, 0, 0.0  # zeroed fields: plain routing, scale 1
+    assert binding.check_config(c) == binding.OK
 
 
 def test_debug_flags_accepted():

@@ -84,3 +84,54 @@ def test_parity_with_a_shared_gate(name, rows):
     check_against_oracle(g, o, cfg)
     plain = oracle.moe_tail(x, r, weights(name), cfg)
     assert not np.allclose(plain["y_shared"], o["y_shared"])  # the gate changed the shared part
+
+
+def _grouped_rows(cfg, w, max_attempts=64):
+    """Rows whose group ranking and kept top-k are both well posed: the
+    topk_group-th and next group scores, and the K-th and next keys among the
+    kept experts, differ by at least 1e-4 relative (oracle keys, double)."""
+    from cases import GAP_REL, key_gaps
+
+    gs = cfg.experts // cfg.n_group
+    xs, rs = [], []
+    for row in range(cfg.rows):
+        for a in range(max_attempts):
+            x, res = synth.make_row(cfg, row, a, 0.0)
+            _, ky = oracle.router_keys(x[None], res[None], w, cfg)
+            k = ky[0]
+            sc = -np.sort(-k.reshape(cfg.n_group, gs), axis=1)[:, :2].sum(axis=1)
+            s = np.sort(sc)[::-1]
+            t = cfg.topk_group
+            gap_g = np.inf if t >= cfg.n_group else (s[t - 1] - s[t]) / max(abs(s[t - 1]), abs(s[t]), 1e-300)
+            kept = np.argsort(-sc, kind="stable")[:t]
+            kk = np.concatenate([k[g * gs:(g + 1) * gs] for g in kept])
+            if gap_g >= GAP_REL and key_gaps(kk[None], cfg.topk)[0] >= GAP_REL:
+                break
+        else:
+            raise RuntimeError("no well-posed grouped row")
+        xs.append(x)
+        rs.append(res)
+    return np.stack(xs), np.stack(rs)
+
+
+@pytest.mark.parametrize("name,rows,n_group,topk_group,scale", [
+    ("c0", 2, 2, 1, 1.0), ("c1", 8, 8, 3, 1.0), ("c3", 4, 8, 4, 2.5)])
+def test_parity_grouped_routing_and_routed_scale(name, rows, n_group, topk_group, scale):
+    """Group-limited top-k and a routed scaling factor on the GPU against the
+    oracle: one lane per group (c0), 8 lanes per group with softmax keys (c1
+    at 8 rows), sigmoid keys with a selection bias and a scale of 2.5 (c3)."""
+    import dataclasses
+
+    cfg = dataclasses.replace(synth.CONFIGS[name].with_rows(rows), n_group=n_group, topk_group=topk_group,
+                              routed_scale=scale)
+    _say("grouped", name, rows, n_group, topk_group, scale)
+    w = weights(name)
+    x, r = _grouped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    h = handle_for(cfg)
+    g = run(h, cfg, device_weights(name), x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    gs = cfg.experts // n_group
+    for row in range(rows):
+        assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
