@@ -63,6 +63,7 @@ class Config:
     n_group: int = 1  # group-limited routing: expert groups (1: none)
     topk_group: int = 1  # groups kept
     routed_scale: float = 1.0  # routed scaling factor on the top-k weights
+    weight_format: int = 0  # routed experts: 0 MXFP4 (E2M1 codes), 1 MXFP8 (E4M3 codes); E8M0 block-32 scales
     seed: int = 0
 
     def with_rows(self, rows: int) -> "Config":
@@ -98,6 +99,11 @@ def _rand_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return np.frombuffer(bytearray(rng.bytes(n)), dtype=np.uint8).reshape(shape)
 
 
+def _e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    v = rng.integers(0, 254, size=shape)
+    return (v + (v >= 0x7F)).astype(np.uint8)
+
+
 def make_weights(cfg: Config, experts: Optional[int] = None) -> dict:
     """All weights of one rank's shard, in the layouts the C ABI takes.
 
@@ -110,9 +116,15 @@ def make_weights(cfg: Config, experts: Optional[int] = None) -> dict:
     H, I, Is = cfg.hidden, cfg.inter, cfg.shared_inter
     std = 1.0 / math.sqrt(H)
     w = make_router_weights(cfg, experts)
-    w["w13_q"] = _rand_bytes(_rng(cfg, _S_W13Q), (E, 2 * I, H // 2))
+    if cfg.weight_format == 1:  # E4M3 codes uniform over the 254 that are not NaN (0x7F, 0xFF)
+        w["w13_q"] = _e4m3_codes(_rng(cfg, _S_W13Q), (E, 2 * I, H))
+    else:
+        w["w13_q"] = _rand_bytes(_rng(cfg, _S_W13Q), (E, 2 * I, H // 2))
     w["w13_s"] = (127 + _rng(cfg, _S_W13S).integers(-6, -2, size=(E, 2 * I, H // 32))).astype(np.uint8)
-    w["w2_q"] = _rand_bytes(_rng(cfg, _S_W2Q), (E, H, I // 2))
+    if cfg.weight_format == 1:
+        w["w2_q"] = _e4m3_codes(_rng(cfg, _S_W2Q), (E, H, I))
+    else:
+        w["w2_q"] = _rand_bytes(_rng(cfg, _S_W2Q), (E, H, I // 2))
     w["w2_s"] = (127 + _rng(cfg, _S_W2S).integers(-6, -2, size=(E, H, I // 32))).astype(np.uint8)
     if Is > 0:
         w["ws13"] = to_bf16_bits(_rng(cfg, _S_WS13).standard_normal((2 * Is, H), dtype=np.float32) * std)

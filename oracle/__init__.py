@@ -59,7 +59,9 @@ def lib():
         L.oracle_norm_row.restype = None
         L.oracle_norm_row.argtypes = [i, d, p, p, p, p, p, p]
         L.oracle_moe_tail.restype = i
-        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d, i, i, d] + [p] * 21
+        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d, i, i, d, i] + [p] * 21
+        L.oracle_e4m3.restype = d
+        L.oracle_e4m3.argtypes = [i]
         L.oracle_topk_grouped.restype = None
         L.oracle_topk_grouped.argtypes = [i, i, p, i, i, p]
         L.oracle_router_keys.restype = i
@@ -100,6 +102,10 @@ def topk(keys: np.ndarray, k: int) -> np.ndarray:
     ids = np.zeros(k, dtype=np.int32)
     lib().oracle_topk(keys.size, k, _ptr(keys), _ptr(ids))
     return ids
+
+
+def e4m3(code: int) -> float:
+    return lib().oracle_e4m3(code)
 
 
 def topk_grouped(keys: np.ndarray, k: int, n_group: int, topk_group: int) -> np.ndarray:
@@ -169,6 +175,7 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
     rc = lib().oracle_moe_tail(
         R, H, E, K, I, Is, cfg.scoring, float(np.float32(cfg.eps)), getattr(cfg, "n_group", 1),
         getattr(cfg, "topk_group", 1), float(np.float32(getattr(cfg, "routed_scale", 1.0))),
+        getattr(cfg, "weight_format", 0),
         _ptr(np.ascontiguousarray(x)), _ptr(None if r is None else np.ascontiguousarray(r)), _ptr(w["gamma"]),
         _ptr(w["router_w"]), _ptr(w.get("router_bias")), _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w2_q"]),
         _ptr(w["w2_s"]), _ptr(w.get("ws13")), _ptr(w.get("ws2")), _ptr(w.get("shared_gate")), _ptr(o["h"]),

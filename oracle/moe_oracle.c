@@ -19,6 +19,7 @@
  *   w      = softmax(l[S])     (softmax scoring; equals p[S]/sum p[S])
  *          = sigmoid(l[S]) / sum sigmoid(l[S])   (sigmoid scoring)
  *            times the routed scaling factor (1 unless given)
+ *   deq    = E2M1 x E8M0 (MXFP4) or E4M3 x E8M0 (MXFP8), blocks of 32
  *   for each pick e in S:  [g | u] = deq(W13[e]) xn,  a = g*sigmoid(g)*u,
  *                          d_e = deq(W2[e]) a
  *   s      = Ws2 (silu(Ws13_gate xn) * Ws13_up xn)   bf16 shared expert
@@ -62,6 +63,15 @@ double oracle_e2m1(int code) {
 double oracle_e8m0(int b) {
   if ((b & 0xFF) == 0xFF) return NAN;
   return ldexp(1.0, (b & 0xFF) - 127);
+}
+
+/* E4M3 (OCP MX v1.0 FP8): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities. */
+double oracle_e4m3(int code) {
+  const int s = (code >> 7) & 1, e = (code >> 3) & 0xF, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
 }
 
 double oracle_dequant(int code, int scale_byte) {
@@ -211,31 +221,34 @@ void oracle_topk_weights(int K, int scoring, const double* logits, const int32_t
   for (int k = 0; k < K; k++) w[k] /= sum;
 }
 
-/* Dequantized MXFP4 element (row, col) of a [rows, cols] matrix stored as
- * codes [rows, cols/2] (low nibble = even column) and scales [rows, cols/32]. */
-static double mx_at(const uint8_t* q, const uint8_t* s, int cols, int row, int col) {
+/* Dequantized element (row, col) of a [rows, cols] matrix with scales
+ * [rows, cols/32].  MXFP4 (fmt 0): codes [rows, cols/2], low nibble = even
+ * column.  MXFP8 (fmt 1): E4M3 codes [rows, cols], one byte per element. */
+static double mx_at(int fmt, const uint8_t* q, const uint8_t* s, int cols, int row, int col) {
+  const double sc = oracle_e8m0(s[(size_t)row * (cols / 32) + col / 32]);
+  if (fmt == 1) return oracle_e4m3(q[(size_t)row * cols + col]) * sc;
   uint8_t byte = q[(size_t)row * (cols / 2) + col / 2];
   int code = (col & 1) ? (byte >> 4) : (byte & 0xF);
-  return oracle_dequant(code, s[(size_t)row * (cols / 32) + col / 32]);
+  return oracle_e2m1(code) * sc;
 }
 
 /* One routed expert on one row: d[H] = W2 (silu(g) * u), [g|u] = W13 xn. */
-void oracle_expert_row(int H, int I, const uint16_t* xn, const uint8_t* w13_q, const uint8_t* w13_s,
+void oracle_expert_row(int fmt, int H, int I, const uint16_t* xn, const uint8_t* w13_q, const uint8_t* w13_s,
                        const uint8_t* w2_q, const uint8_t* w2_s, double* a_out, double* d_out) {
   double* a = (double*)malloc(sizeof(double) * (size_t)I);
   for (int i = 0; i < I; i++) {
     double g = 0.0, u = 0.0;
     for (int j = 0; j < H; j++) {
       double v = bfd(xn, j);
-      g += mx_at(w13_q, w13_s, H, i, j) * v;
-      u += mx_at(w13_q, w13_s, H, I + i, j) * v;
+      g += mx_at(fmt, w13_q, w13_s, H, i, j) * v;
+      u += mx_at(fmt, w13_q, w13_s, H, I + i, j) * v;
     }
     a[i] = g * sigmoid(g) * u;
     if (a_out) a_out[i] = a[i];
   }
   for (int h = 0; h < H; h++) {
     double acc = 0.0;
-    for (int i = 0; i < I; i++) acc += mx_at(w2_q, w2_s, I, h, i) * a[i];
+    for (int i = 0; i < I; i++) acc += mx_at(fmt, w2_q, w2_s, I, h, i) * a[i];
     d_out[h] = acc;
   }
   free(a);
@@ -274,7 +287,7 @@ double oracle_shared_gate(int H, const uint16_t* xn, const uint16_t* wg) {
  * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H].  sgate [H]
  * may be NULL (no shared gate); y_shared is the gated shared output. */
 int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps, int n_group,
-                    int topk_group, double routed_scale,
+                    int topk_group, double routed_scale, int wfmt,
                     const uint16_t* x, const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w,
                     const float* bias, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                     const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, const uint16_t* sgate,
@@ -283,6 +296,7 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
                     double* y_routed_out, double* y_shared_out, uint16_t* out) {
   if (rows < 0 || H <= 0 || H % 32 || E <= 0 || K <= 0 || K > E || I <= 0 || I % 32 || Is < 0 || !out) return 1;
   if (scoring == 1 && !bias) return 1;
+  if (wfmt != 0 && wfmt != 1) return 1;
   if (n_group > 1 && (E % n_group || topk_group < 1 || topk_group > n_group || K > topk_group * (E / n_group)))
     return 1;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
@@ -294,8 +308,8 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
   double* d = (double*)malloc(sizeof(double) * (size_t)H);
   double* yr = (double*)malloc(sizeof(double) * (size_t)H);
   double* ys = (double*)malloc(sizeof(double) * (size_t)H);
-  const size_t e13 = (size_t)2 * I * (H / 2), e13s = (size_t)2 * I * (H / 32);
-  const size_t e2 = (size_t)H * (I / 2), e2s = (size_t)H * (I / 32);
+  const size_t e13 = (size_t)2 * I * (wfmt == 1 ? H : H / 2), e13s = (size_t)2 * I * (H / 32);
+  const size_t e2 = (size_t)H * (wfmt == 1 ? I : I / 2), e2s = (size_t)H * (I / 32);
   for (int row = 0; row < rows; row++) {
     const size_t ro = (size_t)row * H;
     oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
@@ -307,7 +321,7 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
     for (int j = 0; j < H; j++) yr[j] = 0.0;
     for (int k = 0; k < K; k++) {
       const int e = ids[k];
-      oracle_expert_row(H, I, xn, w13_q + e * e13, w13_s + e * e13s, w2_q + e * e2, w2_s + e * e2s, NULL, d);
+      oracle_expert_row(wfmt, H, I, xn, w13_q + e * e13, w13_s + e * e13s, w2_q + e * e2, w2_s + e * e2s, NULL, d);
       for (int j = 0; j < H; j++) yr[j] += w[k] * d[j];
     }
     for (int j = 0; j < H; j++) ys[j] = 0.0;

@@ -497,3 +497,61 @@ def test_grouped_routing_in_the_tail_keeps_picks_inside_the_kept_groups():
         top2 = -np.sort(-ky, axis=1)[:, :2].sum(axis=1)
         kept = set(np.argsort(-top2, kind="stable")[:2].tolist())
         assert {int(e) // 4 for e in og["ids"][row]} <= kept
+
+
+# ---- a second expert weight format: MXFP8 (E4M3 codes, E8M0 block-32 scales,
+# OCP Microscaling Formats v1.0) ---------------------------------------------
+
+def test_e4m3_anchor_values_of_the_spec():
+    """OCP MX v1.0 FP8 E4M3: max normal 448 (0x7E), min normal 2^-6 (0x08),
+    min subnormal 2^-9 (0x01), 1.0 = 0x38, NaN at S.1111.111, signed zeros."""
+    assert oracle.e4m3(0x7E) == 448.0
+    assert oracle.e4m3(0xFE) == -448.0
+    assert oracle.e4m3(0x08) == 2.0 ** -6
+    assert oracle.e4m3(0x01) == 2.0 ** -9
+    assert oracle.e4m3(0x38) == 1.0
+    assert np.isnan(oracle.e4m3(0x7F)) and np.isnan(oracle.e4m3(0xFF))
+    assert oracle.e4m3(0x00) == 0.0 and oracle.e4m3(0x80) == 0.0
+
+
+def test_e4m3_every_code_from_its_bit_fields():
+    """Each non-NaN code rebuilt as an fp32 bit pattern: a normal code moves its
+    exponent (bias 7 -> 127) and mantissa (3 -> 23 bits) into place; a
+    subnormal one is m * 2^-9."""
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            continue
+        s, e, m = code >> 7, (code >> 3) & 0xF, code & 7
+        if e:
+            bits = (s << 31) | ((e - 7 + 127) << 23) | (m << 20)
+            want = float(np.array([bits], np.uint32).view(np.float32)[0])
+        else:
+            want = (-1.0) ** s * m * 2.0 ** -9
+        assert oracle.e4m3(code) == want, hex(code)
+
+
+def test_mxfp8_copy_of_mxfp4_weights_gives_the_same_tail():
+    """Every E2M1 value is exact in E4M3.  MXFP4 weights re-encoded as MXFP8
+    (one byte per element, same scales) give the same tail, bit for bit: this
+    pins the MXFP8 layout (row strides, one byte per element) and its decode."""
+    import dataclasses
+
+    cfg = synth.CONFIGS["c0"].with_rows(2)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    o4 = oracle.moe_tail(x, r, w, cfg)
+    to8 = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C], np.uint8)  # E2M1 magnitudes as E4M3
+
+    def unpack(q):
+        lo, hi = q & 0xF, q >> 4
+        codes = np.stack([lo, hi], axis=-1).reshape(q.shape[:-1] + (q.shape[-1] * 2,))
+        return to8[codes & 7] | ((codes & 8) << 4).astype(np.uint8)
+
+    w8 = dict(w)
+    w8["w13_q"] = unpack(w["w13_q"])
+    w8["w2_q"] = unpack(w["w2_q"])
+    for c in range(16):  # the re-encoding itself is exact
+        assert oracle.e4m3(int(to8[c & 7] | ((c & 8) << 4))) == oracle.e2m1(c)
+    o8 = oracle.moe_tail(x, r, w8, dataclasses.replace(cfg, weight_format=1))
+    for k in ("ids", "w", "y_routed", "y_shared", "out"):
+        np.testing.assert_array_equal(o8[k], o4[k])
