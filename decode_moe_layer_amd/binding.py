@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_tail.so")
 
 OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ETIMEOUT = 0, 1, 2, 3, 4, 5
 SOFTMAX, SIGMOID_BIAS = 0, 1
+MXFP4, MXFP8 = 0, 1
 DEBUG_STALL = 1
 DEBUG_STALL_ONCE = 2
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EHIP", 5: "ETIMEOUT"}
@@ -29,6 +30,7 @@ class Config(ctypes.Structure):
         ("scoring", ctypes.c_int32), ("eps", ctypes.c_float), ("device", ctypes.c_int32),
         ("deadline_us", ctypes.c_uint32), ("debug_flags", ctypes.c_uint32), ("debug_block", ctypes.c_int32),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -72,9 +74,9 @@ def lib():
 
 def make_config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring=SOFTMAX, eps=1e-6,
                 device=-1, deadline_us=0, debug_flags=0, debug_block=0, n_group=1, topk_group=1,
-                routed_scale=1.0) -> Config:
+                routed_scale=1.0, weight_format=MXFP4) -> Config:
     return Config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring, eps, device, deadline_us,
-                  debug_flags, debug_block, n_group, topk_group, routed_scale)
+                  debug_flags, debug_block, n_group, topk_group, routed_scale, weight_format)
 
 
 def check_config(cfg: Config) -> int:

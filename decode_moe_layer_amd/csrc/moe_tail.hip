@@ -19,11 +19,25 @@
 //           (chunk-ordered fp32 partials: "Split the Kimi3 AttnRes mix across
 //           CTAs for decode rows", flare PR 11, design section)
 //
-// Cross-workgroup exchange goes through handle-owned scratch: counters in two
-// banks selected by the call's epoch (an atomic ticket / grid size), so no
-// reset is needed between calls or graph replays; every wait has a deadline
-// and a shared abort word (K2 commit text, Motivation: each wait has a
-// deadline, a failed wait stops the launch everywhere).
+// Optional steps (separate kernel variants): the shared expert's output scaled
+// by a sigmoid gate of the normed row (K2 commit text, Kernel Replacement), and
+// group-limited routing with a routed scaling factor; and routed experts in
+// MXFP8 (E4M3 codes, one byte each, with the same E8M0 block-32 scales; the
+// FP8 expert path of PR 85, its commits on 16-byte FP8 loads and on the FP8
+// mid).  An MXFP8 column group is two 16-byte lane loads instead of one,
+// decoded with v_cvt_scalef32_pk_bf16_fp8, exact in bf16 like E2M1; the
+// activations of the down projection stay bf16 (no FP8 re-quantisation of
+// the mid, which would add error beyond the tail's tolerance).
+//
+// Cross-workgroup exchange goes through handle-owned scratch.  Every
+// workgroup counts the calls it has started (its epoch).  On the router chain
+// the data carry the epoch as a tag (xn chunks, router partials, logits), so
+// a reader polls the data themselves; elsewhere counters in two banks,
+// selected by the epoch's parity, release the readers, and no reset is needed
+// between calls or graph replays.  Every wait has a deadline and a shared
+// abort word (K2 commit text, Motivation: each wait has a deadline, a failed
+// wait stops the launch everywhere; "Split the Kimi3 AttnRes mix across CTAs
+// for decode rows", design section: per-call tags in the exchanged words).
 //
 // GEMV tiles use v_mfma_f32_16x16x32_bf16: weights are the A operand (16
 // rows), activations the B operand (up to 16 rows as columns), staged in LDS.
@@ -98,6 +112,7 @@ struct Ctl {
 struct Params {
   int R, H, E, K, I, Is, scoring, G;
   int n_group, topk_group;  // group-limited routing (n_group 1: none)
+  int f8;                   // routed experts in MXFP8 (E4M3 codes), else MXFP4
   float rscale;             // routed scaling factor
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
   int rsum;                       // top-k readers sum the router K-chunk partials themselves
@@ -178,16 +193,9 @@ template <int CP>
 __device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP);
 }
-template <int CP>
-__device__ __forceinline__ uint32_t ld1(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, CP);
-}
 __device__ __forceinline__ void stc16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
                                          r, (int)off, 0, CP_SC1);
-}
-__device__ __forceinline__ void stcf(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, CP_SC1);
 }
 __device__ __forceinline__ void stc2(rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, CP_SC1);
@@ -223,6 +231,16 @@ __device__ __forceinline__ bf16x8 fp4x8(uint32_t v, float scale) {
   return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 8 E4M3 codes (two dwords, element 0 in the low byte) -> 8 bf16 times scale
+// (E4M3 x 2^(s-127) is exact in bf16 for the scales in range)
+__device__ __forceinline__ bf16x8 fp8x8(uint32_t lo, uint32_t hi, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+  return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -255,16 +273,11 @@ __device__ __forceinline__ int dpp(int id, int v) {
   v = OP(v, dpp<0x142, 0xA>((ID), (v)));       \
   v = OP(v, dpp<0x143, 0xC>((ID), (v)));
 __device__ __forceinline__ int umax_(int a, int b) { return (uint32_t)a > (uint32_t)b ? a : b; }
-__device__ __forceinline__ int imin_(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int fadd_(int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   int v = (int)x;
   WAVE_REDUCE(v, umax_, 0)
   return (uint32_t)__builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ int wave_min_i32(int v) {
-  WAVE_REDUCE(v, imin_, 0x7FFFFFFF)
-  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ float wave_sum_f32(float x) {
   int v = __float_as_int(x);
@@ -449,24 +462,19 @@ __device__ unsigned long long g_timeline[1024 * TL_N];
 struct FragA {  // one 16-byte weight load per lane
   u32x4 a;
 };
-struct FragAB {  // weight + activation loads (activations from global scratch)
-  u32x4 a, b;
-};
-struct FragQ {  // MXFP4: codes + the 4 block scales of this instruction's chunks
-  u32x4 a;
-  uint32_t s;
-};
 struct FragU {  // MXFP4: up to 8 column groups of one unit, with their block-scale dwords
   u32x4 a[8];
   u32x4 s[2];
 };
-struct FragQB {
-  u32x4 a;
+template <bool F8>
+struct FragQB {  // one column group (one 16-byte load of MXFP4 codes, two of MXFP8) with its B fragments
+  u32x4 a[F8 ? 2 : 1];
   uint32_t s;
   u32x4 b[4];
 };
-struct FragD {  // MXFP4 down: 2 column groups x both row blocks, with the dwords holding their block scales
-  u32x4 a[2][MAX_BLK];
+template <bool F8>
+struct FragD {  // down: 2 column groups x both row blocks (x 2 halves for MXFP8), with their scale dwords
+  u32x4 a[2][F8 ? 2 : 1][MAX_BLK];
   uint32_t s[MAX_BLK][2];
 };
 struct FragSD {
@@ -500,7 +508,7 @@ constexpr int RED_FLOATS = 2 * NW * 64 * 4;  // floats in Shared::red
 
 // ------------------------------------------------------------------ kernel --
 
-template <bool XL, bool RS, bool FEAT>
+template <bool XL, bool RS, bool FEAT, bool F8>
 __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int tid = threadIdx.x, lane = tid & 63, cta = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -1057,7 +1065,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW, t02 = wave * TP2;
     const int u0 = cta;
     const int nu2 = u0 < n_p2 ? (n_p2 - 1 - u0) / G + 1 : 0;
-    const size_t S13 = (size_t)2 * I * (H / 2), S13s = (size_t)2 * I * (H / 32);
+    // codes per expert: MXFP4 packs two per byte, MXFP8 one
+    const int RB13 = F8 ? H : H / 2;
+    const size_t S13 = (size_t)2 * I * RB13, S13s = (size_t)2 * I * (H / 32);
     int rb = 0;
     // end of unit u: reduce the 8 waves' partials in wave order; a = silu(gate) * up
     auto p2_reduce = [&](f32x4 acc, int u) {
@@ -1083,7 +1093,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       // the block-scale dwords of those column groups (lane (i16, g) loads dwords
       // tb .. tb+7 of its row; column group tb + tt uses dword tt, byte g), so a
       // unit costs one or two scale loads instead of one per column group.
-      const int NP = (TP2 + 7) / 8;
+      // an MXFP8 column group takes two 16-byte loads, so a frag holds 4 of them
+      constexpr int CPF = F8 ? 4 : 8;
+      const int NP = (TP2 + CPF - 1) / CPF;
       int k2 = 0, q2 = 0;
       auto p2_next = [&]() {
         FragU f;
@@ -1093,11 +1105,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const rsrc_t rq = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
         const rsrc_t rs = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
         const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
-        const int tb = t02 + 8 * q2, np = min(8, TP2 - 8 * q2);
-        const uint32_t qoff = (uint32_t)(wrow * (H / 2) + g * 16), soff = (uint32_t)(wrow * (H / 32) + tb * 4);
+        const int tb = t02 + CPF * q2, np = min(CPF, TP2 - CPF * q2);
+        const uint32_t qoff = (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16)), soff = (uint32_t)(wrow * (H / 32) + tb * 4);
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          f.a[t] = ld16<CP_W>(rq, (v && t < np && tb + t < T2) ? qoff + (uint32_t)(tb + t) * 64u : OOB);
+        for (int j = 0; j < 8; ++j) {
+          const int t = F8 ? j >> 1 : j;
+          const uint32_t o = F8 ? (uint32_t)(tb + t) * 128u + (uint32_t)(j & 1) * 16u : (uint32_t)(tb + t) * 64u;
+          f.a[j] = ld16<CP_W>(rq, (v && t < np && tb + t < T2) ? qoff + o : OOB);
+        }
         f.s[0] = ld16<CP_W>(rs, v ? soff : OOB);
         f.s[1] = ld16<CP_W>(rs, (v && np > 4) ? soff + 16u : OOB);
         if (++q2 == NP) {
@@ -1115,9 +1130,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const int u = u0 + kk * G, d = u / UB;
         const uint32_t mask = S.slot_mask[d];
         const int brow = (i16 < __popc(mask) ? nth_bit(mask, i16) : xzero) * p.xs + g * 32;
-        const int tb = t02 + 8 * qc, np = min(8, TP2 - 8 * qc);
+        const int tb = t02 + CPF * qc, np = min(CPF, TP2 - CPF * qc);
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
+        for (int tt = 0; tt < CPF; ++tt) {
           if (tt < np) {
             const int t = tb + tt;
             const float sc = e8m0f((f.s[tt >> 2][tt & 3] >> (8 * g)) & 0xFFu);
@@ -1125,7 +1140,11 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) bq[q] = lds16(xl + (t < T2 ? brow + t * 128 + 8 * q : xzero * p.xs));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[tt][q], sc), as_bf16x8(bq[q]), acc);
+            for (int q = 0; q < 4; ++q) {
+              const bf16x8 aq = F8 ? fp8x8(f.a[2 * tt + (q >> 1)][2 * (q & 1)], f.a[2 * tt + (q >> 1)][2 * (q & 1) + 1], sc)
+                                   : fp4x8(f.a[tt][q], sc);
+              acc = mfma(aq, as_bf16x8(bq[q]), acc);
+            }
           }
         }
         if (++qc == NP) {
@@ -1147,16 +1166,18 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
         rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
         const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
-        qoff = (uint32_t)(wrow * (H / 2) + g * 16);
+        qoff = (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
         soff = (uint32_t)(wrow * (H / 32));
         const uint32_t mask = S.slot_mask[d];
         boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
       };
       if (nu2) p2_unit();
       auto p2_next = [&]() {
-        FragQB f;
+        FragQB<F8> f;
         const bool v = k2 < nu2 && t2 < T2;
-        f.a = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * 64u : OOB);
+#pragma unroll
+        for (int j = 0; j < (F8 ? 2 : 1); ++j)
+          f.a[j] = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * (F8 ? 128u : 64u) + (uint32_t)j * 16u : OOB);
         f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -1167,15 +1188,19 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         }
         return f;
       };
-      Window<D_FP4_G, FragQB> w2;
+      Window<D_FP4_G, FragQB<F8>> w2;
       w2.prime(p2_next);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       int kk = 0, tt = 0;
       if (nu2 && TL_ON) TL(13);
-      w2.run(nu2 * TP2, p2_next, [&](const FragQB& f) {
+      w2.run(nu2 * TP2, p2_next, [&](const FragQB<F8>& f) {
         const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = mfma(fp4x8(f.a[q], sc), as_bf16x8(f.b[q]), acc);
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 aq = F8 ? fp8x8(f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1)], f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1) + 1], sc)
+                               : fp4x8(f.a[0][q], sc);
+          acc = mfma(aq, as_bf16x8(f.b[q]), acc);
+        }
         if (++tt == TP2) {
           tt = 0;
           p2_reduce(acc, u0 + kk * G);
@@ -1193,7 +1218,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int nblk = (hn + 15) / 16;
   const int CI = I / 32, TI = (CI + 3) / 4;
   const int nsl = D > wave ? (D - wave + NW - 1) / NW : 0;
-  const size_t S2 = (size_t)H * (I / 2), S2s = (size_t)H * CI;
+  const int RB2 = F8 ? I : I / 2;  // down code bytes per hidden row
+  const size_t S2 = (size_t)H * RB2, S2s = (size_t)H * CI;
   uint16_t* al = (uint16_t*)dyn;                // [P + 1][as] routed a; row azero is zeros
   uint16_t* asl = (uint16_t*)(dyn + p.off_as);  // [R + 1][ss] shared a; row szero is zeros
   float* s_outp = (float*)(dyn + p.off_outp);   // [P][HR]
@@ -1208,14 +1234,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int s3r = (h0 * CI) & 3;  // slice start mod 4 (expert strides H CI are multiples of 4)
   int j3 = 0, q3 = 0;
   auto p3_next = [&]() {
-    FragD f;
+    FragD<F8> f;
     const bool v = j3 < nsl && hn > 0;
     const int e = v ? __builtin_amdgcn_readfirstlane(S.slot_expert[wave + NW * j3]) : 0;  // uniform
     // scale bytes from a 4-byte aligned base at or below the slice start; the
     // dword loads stay inside the array (its size is a multiple of 4)
     const size_t so = (size_t)e * S2s + (size_t)h0 * CI, sa = so & ~(size_t)3;
     const uint32_t sr = (uint32_t)(so - sa);
-    const rsrc_t rq = make_rsrc_u(p.w2q + e * S2 + (size_t)h0 * (I / 2), (uint32_t)(hn * (I / 2)));
+    const rsrc_t rq = make_rsrc_u(p.w2q + e * S2 + (size_t)h0 * RB2, (uint32_t)(hn * RB2));
     const rsrc_t rs = make_rsrc_u(p.w2s + sa, (uint32_t)((size_t)E * H * CI - sa));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1224,7 +1250,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       for (int bl = 0; bl < MAX_BLK; ++bl) {
         const int hh = 16 * bl + i16;
         const bool ok = v && t3 < TI && bl < nblk && hh < hn && c < CI;
-        f.a[t][bl] = ld16<CP_W>(rq, ok ? (uint32_t)(hh * (I / 2) + c * 16) : OOB);
+#pragma unroll
+        for (int j = 0; j < (F8 ? 2 : 1); ++j)
+          f.a[t][j][bl] = ld16<CP_W>(rq, ok ? (uint32_t)(hh * RB2 + c * (F8 ? 32 : 16) + j * 16) : OOB);
         f.s[bl][t] = ld4<CP_W>(rs, ok ? (sr + (uint32_t)(hh * CI + c)) & ~3u : OOB);
       }
     }
@@ -1254,7 +1282,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     __syncthreads();
   }
-  Window<2, FragD> w3;
+  Window<2, FragD<F8>> w3;
   w3.prime(p3_next);
   TL(9);
   if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
@@ -1349,7 +1377,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
     int ju = 0, qu = 0;
-    w3.run(nsl * NP3, p3_next, [&](const FragD& f) {
+    w3.run(nsl * NP3, p3_next, [&](const FragD<F8>& f) {
       const int d = wave + NW * ju;
       const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
       const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
@@ -1366,7 +1394,12 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
               const uint32_t sb = f.s[bl][t] >> (8 * ((s3r + (16 * bl + i16) * CI + c) & 3));
               const float sc = e8m0f(sb & 0xFFu);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) acc[bl] = mfma(fp4x8(f.a[t][bl][q], sc), as_bf16x8(b[q]), acc[bl]);
+              for (int q = 0; q < 4; ++q) {
+                const bf16x8 aq = F8 ? fp8x8(f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1)],
+                                             f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1) + 1], sc)
+                                     : fp4x8(f.a[t][0][bl][q], sc);
+                acc[bl] = mfma(aq, as_bf16x8(b[q]), acc[bl]);
+              }
             }
           }
         }
@@ -1413,20 +1446,28 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 // _f kernels add the optional steps (the shared expert's gate, group-limited
 // routing).  A call runs its code once, front to back, so code it does not
 // execute still costs instruction fetches: the plain kernels carry none of it.
-#define MT_KERNEL(NAME, XL, RS, FEAT)                            \
+#define MT_KERNEL(NAME, XL, RS, FEAT, F8)                        \
   __global__ __launch_bounds__(NT, 1) void NAME(Params p) {      \
     __shared__ Shared S;                                         \
     extern __shared__ __attribute__((aligned(16))) char s_dyn[]; \
-    tail<XL, RS, FEAT>(p, S, s_dyn);                             \
+    tail<XL, RS, FEAT, F8>(p, S, s_dyn);                         \
   }
-MT_KERNEL(moe_tail_kernel_lds, true, false, false)
-MT_KERNEL(moe_tail_kernel_lds_rs, true, true, false)
-MT_KERNEL(moe_tail_kernel_gm, false, false, false)
-MT_KERNEL(moe_tail_kernel_lds_f, true, false, true)
-MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true)
-MT_KERNEL(moe_tail_kernel_gm_f, false, false, true)
+MT_KERNEL(moe_tail_kernel_lds, true, false, false, false)
+MT_KERNEL(moe_tail_kernel_lds_rs, true, true, false, false)
+MT_KERNEL(moe_tail_kernel_gm, false, false, false, false)
+MT_KERNEL(moe_tail_kernel_lds_f, true, false, true, false)
+MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true, false)
+MT_KERNEL(moe_tail_kernel_gm_f, false, false, true, false)
+// MXFP8 experts (E4M3 codes), with the optional steps
+MT_KERNEL(moe_tail_kernel_lds_f8, true, false, true, true)
+MT_KERNEL(moe_tail_kernel_lds_rs_f8, true, true, true, true)
+MT_KERNEL(moe_tail_kernel_gm_f8, false, false, true, true)
 #undef MT_KERNEL
 static const void* kernel_for(const Params& p) {
+  if (p.f8) {
+    if (!p.xn_lds) return (const void*)moe_tail_kernel_gm_f8;
+    return p.rsum ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_f8;
+  }
   const bool f = p.sgate || p.n_group > 1;
   if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f : (const void*)moe_tail_kernel_gm;
   if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f : (const void*)moe_tail_kernel_lds_rs;
@@ -1534,6 +1575,8 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
                          c->top_k > c->topk_group * (c->num_experts / c->n_group)))
     return fail(nullptr, MOE_TAIL_EINVAL, "topk_group %d must be in 1..n_group and keep at least top_k experts",
                 c->topk_group);
+  if (c->weight_format != MOE_TAIL_MXFP4 && c->weight_format != MOE_TAIL_MXFP8)
+    return fail(nullptr, MOE_TAIL_EINVAL, "unknown weight_format %d", c->weight_format);
   if (!(c->routed_scale >= 0.f) || !isfinite(c->routed_scale))
     return fail(nullptr, MOE_TAIL_EINVAL, "routed_scale must be finite and not negative");
   if (c->debug_flags & ~(MOE_TAIL_DEBUG_STALL | MOE_TAIL_DEBUG_STALL_ONCE))
@@ -1612,10 +1655,12 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   }
   e = hipMemset(h->scratch, 0, total);
   {
-    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds, (const void*)mt::moe_tail_kernel_lds_rs,
-                        (const void*)mt::moe_tail_kernel_lds_f, (const void*)mt::moe_tail_kernel_lds_rs_f,
-                        (const void*)mt::moe_tail_kernel_gm, (const void*)mt::moe_tail_kernel_gm_f};
-    for (int k = plan.xn_lds ? 0 : 4; k < (plan.xn_lds ? 4 : 6) && e == hipSuccess; ++k)
+    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds,     (const void*)mt::moe_tail_kernel_lds_rs,
+                        (const void*)mt::moe_tail_kernel_lds_f,   (const void*)mt::moe_tail_kernel_lds_rs_f,
+                        (const void*)mt::moe_tail_kernel_lds_f8,  (const void*)mt::moe_tail_kernel_lds_rs_f8,
+                        (const void*)mt::moe_tail_kernel_gm,      (const void*)mt::moe_tail_kernel_gm_f,
+                        (const void*)mt::moe_tail_kernel_gm_f8};
+    for (int k = plan.xn_lds ? 0 : 6; k < (plan.xn_lds ? 6 : 9) && e == hipSuccess; ++k)
       e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -1679,6 +1724,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.n_group = c.n_group > 1 ? c.n_group : 1;
   p.topk_group = c.n_group > 1 ? c.topk_group : 1;
   p.rscale = c.routed_scale > 0.f ? c.routed_scale : 1.f;
+  p.f8 = c.weight_format == MOE_TAIL_MXFP8;
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
   // reader-side router sums when each thread then loads at most 8 partials

@@ -100,8 +100,9 @@ def _rand_bytes(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def _e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
-    v = rng.integers(0, 254, size=shape)
-    return (v + (v >= 0x7F)).astype(np.uint8)
+    v = rng.integers(0, 254, size=shape, dtype=np.uint8)
+    v += v >= 0x7F  # skip 0x7F; 0xFF is never drawn
+    return v
 
 
 def make_weights(cfg: Config, experts: Optional[int] = None) -> dict:

@@ -53,6 +53,12 @@ typedef enum {
 
 typedef enum { MOE_TAIL_SOFTMAX = 0, MOE_TAIL_SIGMOID_BIAS = 1 } moe_tail_scoring;
 
+/* Routed expert weight formats (OCP Microscaling Formats v1.0), both with one
+ * E8M0 scale per 32 elements along K: MXFP4 packs two E2M1 codes per byte
+ * (w13_q [E, 2I, H/2], w2_q [E, H, I/2]); MXFP8 has one E4M3 code per byte
+ * (w13_q [E, 2I, H], w2_q [E, H, I]). */
+typedef enum { MOE_TAIL_MXFP4 = 0, MOE_TAIL_MXFP8 = 1 } moe_tail_weight_format;
+
 /* debug_flags bit: the workgroup `debug_block` never proceeds past its first
  * cross-workgroup wait until that wait's deadline fires (fault drill). */
 #define MOE_TAIL_DEBUG_STALL 1u
@@ -81,6 +87,7 @@ typedef struct {
                            top-k is taken among their experts.  0 or 1: no groups */
   int32_t topk_group;   /* groups kept, 1..n_group, with K <= topk_group * E / n_group */
   float routed_scale;   /* routed scaling factor on the top-k weights; 0 means 1 */
+  int32_t weight_format; /* routed expert codes: MOE_TAIL_MXFP4 (0) or MOE_TAIL_MXFP8 (1) */
 } moe_tail_config;
 
 typedef struct {

@@ -135,3 +135,58 @@ def test_parity_grouped_routing_and_routed_scale(name, rows, n_group, topk_group
     gs = cfg.experts // n_group
     for row in range(rows):
         assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 1), ("c1", 8), ("c4", 16)])
+def test_parity_mxfp8_experts(name, rows):
+    """MXFP8 routed experts (E4M3 codes, one E8M0 scale per 32 elements; OCP
+    Microscaling Formats v1.0) against the oracle on the three kernel paths:
+    routed sums by every reader (c0), xn in LDS (c1 at 8 rows), xn read from
+    global scratch (c4 at 16 rows)."""
+    import dataclasses
+
+    from gpu_harness import dev
+
+    cfg = dataclasses.replace(synth.CONFIGS[name].with_rows(rows), weight_format=1)
+    _say("mxfp8", name, rows)
+    w = synth.make_weights(cfg)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    dw = {k: dev(v) for k, v in w.items()}
+    h = handle_for(cfg)
+    g = run(h, cfg, dw, x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    del dw, h
+
+
+def _fp4_as_fp8(q):
+    """Re-encode packed E2M1 codes (two per byte, low nibble first) as E4M3
+    codes, one per byte; every E2M1 value is exact in E4M3."""
+    to8 = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C], np.uint8)
+    codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[:-1] + (q.shape[-1] * 2,))
+    return to8[codes & 7] | ((codes & 8) << 4).astype(np.uint8)
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 2), ("c1", 8)])
+def test_mxfp8_matches_mxfp4_on_reencoded_weights(name, rows):
+    """The same weights in both formats give the same GPU outputs bit for bit:
+    the MXFP8 loads, strides and decode lane order match the MXFP4 ones."""
+    import dataclasses
+
+    from gpu_harness import dev
+
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    cfg8 = dataclasses.replace(cfg, weight_format=1)
+    _say("fp4-as-fp8", name, rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    g4 = run(handle_for(cfg), cfg, device_weights(name), x, r)
+    dw8 = dict(device_weights(name))
+    dw8["w13_q"] = dev(_fp4_as_fp8(w["w13_q"]))
+    dw8["w2_q"] = dev(_fp4_as_fp8(w["w2_q"]))
+    h8 = handle_for(cfg8)
+    g8 = run(h8, cfg8, dw8, x, r)
+    assert h8.get_error() == 0
+    for k in ("ids", "w", "logits", "y_routed", "y_shared", "out", "res_out"):
+        np.testing.assert_array_equal(g8[k], g4[k], err_msg=k)
