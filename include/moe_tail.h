@@ -97,9 +97,10 @@ typedef struct {
   const void* gamma;        /* [H] bf16 RMSNorm weight */
   const void* router_w;     /* [E, H] bf16 */
   const float* router_bias; /* [E] fp32, required for MOE_TAIL_SIGMOID_BIAS, else ignored */
-  const uint8_t* w13_q;     /* [E, 2I, H/2]: rows [0,I) gate, [I,2I) up; byte j = elements 2j (low nibble), 2j+1 (high) */
+  const uint8_t* w13_q;     /* MXFP4 [E, 2I, H/2]: rows [0,I) gate, [I,2I) up; byte j = elements 2j (low nibble),
+                               2j+1 (high).  MXFP8 [E, 2I, H]: byte j = element j */
   const uint8_t* w13_s;     /* [E, 2I, H/32] E8M0 scale of each 32-element block along H */
-  const uint8_t* w2_q;      /* [E, H, I/2] down projection codes, same nibble order */
+  const uint8_t* w2_q;      /* down projection codes: MXFP4 [E, H, I/2], same nibble order; MXFP8 [E, H, I] */
   const uint8_t* w2_s;      /* [E, H, I/32] E8M0 scales along I */
   const void* ws13;         /* [2Is, H] bf16 shared gate (rows [0,Is)) and up; NULL iff Is == 0 */
   const void* ws2;          /* [H, Is] bf16 shared down; NULL iff Is == 0 */
