@@ -64,6 +64,7 @@ class Config:
     topk_group: int = 1  # groups kept
     routed_scale: float = 1.0  # routed scaling factor on the top-k weights
     weight_format: int = 0  # routed experts: 0 MXFP4 (E2M1 codes), 1 MXFP8 (E4M3 codes); E8M0 block-32 scales
+    fold_norm: int = 0  # 1: rstd multiplies the router and shared gate/up sums over bf16(h * gamma)
     seed: int = 0
 
     def with_rows(self, rows: int) -> "Config":

@@ -59,13 +59,13 @@ def lib():
         L.oracle_norm_row.restype = None
         L.oracle_norm_row.argtypes = [i, d, p, p, p, p, p, p]
         L.oracle_moe_tail.restype = i
-        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d, i, i, d, i] + [p] * 21
+        L.oracle_moe_tail.argtypes = [i, i, i, i, i, i, i, d, i, i, d, i, i] + [p] * 21
         L.oracle_e4m3.restype = d
         L.oracle_e4m3.argtypes = [i]
         L.oracle_topk_grouped.restype = None
         L.oracle_topk_grouped.argtypes = [i, i, p, i, i, p]
         L.oracle_router_keys.restype = i
-        L.oracle_router_keys.argtypes = [i, i, i, i, d] + [p] * 7
+        L.oracle_router_keys.argtypes = [i, i, i, i, d, i] + [p] * 7
         _lib = L
     return _lib
 
@@ -150,7 +150,7 @@ def router_keys(x, r, w: dict, cfg):
     ky = np.zeros((R, cfg.experts), dtype=np.float64)
     bias = w.get("router_bias")
     lib().oracle_router_keys(
-        R, cfg.hidden, cfg.experts, cfg.scoring, float(np.float32(cfg.eps)),
+        R, cfg.hidden, cfg.experts, cfg.scoring, float(np.float32(cfg.eps)), getattr(cfg, "fold_norm", 0),
         _ptr(np.ascontiguousarray(x)), _ptr(None if r is None else np.ascontiguousarray(r)),
         _ptr(w["gamma"]), _ptr(w["router_w"]), _ptr(bias), _ptr(lg), _ptr(ky),
     )
@@ -164,6 +164,8 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
     float64), ids ([R, K] int32), w ([R, K] float64), y_routed, y_shared
     ([R, H] float64).  w may hold "shared_gate" ([H] bf16 bits): the shared
     output is then scaled by sigmoid(shared_gate . xn); y_shared is gated.
+    cfg.fold_norm (if set) folds the norm's rstd into the router and shared
+    gate/up sums, which then project bf16(h * gamma).
     """
     R, H = x.shape
     E, K, I, Is = cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter
@@ -175,7 +177,7 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
     rc = lib().oracle_moe_tail(
         R, H, E, K, I, Is, cfg.scoring, float(np.float32(cfg.eps)), getattr(cfg, "n_group", 1),
         getattr(cfg, "topk_group", 1), float(np.float32(getattr(cfg, "routed_scale", 1.0))),
-        getattr(cfg, "weight_format", 0),
+        getattr(cfg, "weight_format", 0), getattr(cfg, "fold_norm", 0),
         _ptr(np.ascontiguousarray(x)), _ptr(None if r is None else np.ascontiguousarray(r)), _ptr(w["gamma"]),
         _ptr(w["router_w"]), _ptr(w.get("router_bias")), _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w2_q"]),
         _ptr(w["w2_s"]), _ptr(w.get("ws13")), _ptr(w.get("ws2")), _ptr(w.get("shared_gate")), _ptr(o["h"]),

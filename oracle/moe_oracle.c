@@ -24,6 +24,10 @@
  *                          d_e = deq(W2[e]) a
  *   s      = Ws2 (silu(Ws13_gate xn) * Ws13_up xn)   bf16 shared expert
  *   s      = sigmoid(wg . xn) s        only when a shared gate wg [H] is given
+ *   folded norm (optional): the router and the shared gate/up project
+ *            hg = bf16(h * gamma) instead of xn, and rstd multiplies their
+ *            sums: l[e] = rstd * sum_i hg[i] Wr[e, i], likewise g and u of the
+ *            shared expert; the routed experts and the gate still take xn
  *   y      = sum_k w_k d_{S_k} + s ;   out = bf16(h + y)
  *
  * Sources (page titles; no listing is followed line by line):
@@ -36,6 +40,11 @@
  *   - the same K2 commit text, "Kernel Replacement": the shared expert's
  *     output is scaled by a sigmoid gate of the normed row
  *     (_fused_gate_sigmoid_mul_add_kernel); optional here.
+ *   - "glm53: Long-context indexer ..." (sgl-amd-mono PR 86), PR 85's
+ *     commit text (Motivation, and its commit on the router's norm): the
+ *     router keeps bf16(a * gamma) with the sum of squares beside it, and the
+ *     rstd then scales the logits and the activation blocks of the next
+ *     projections (not bitwise equal to projecting the normed row).
  *   - OCP Microscaling Formats (MX) v1.0: E2M1 element and E8M0 scale
  *     encodings, blocks of 32 elements (the pages name MXFP4 but do not
  *     define it).
@@ -254,17 +263,21 @@ void oracle_expert_row(int fmt, int H, int I, const uint16_t* xn, const uint8_t*
   free(a);
 }
 
-/* The bf16 shared expert on one row: s[H]. */
-void oracle_shared_row(int H, int Is, const uint16_t* xn, const uint16_t* ws13, const uint16_t* ws2,
-                       double* s_out) {
+/* The bf16 shared expert on one row: s[H].  Its gate and up sums are taken
+ * over the activation row `act` and then multiplied by `scale` (1 for the
+ * normed row xn; rstd for bf16(h * gamma) when the norm is folded). */
+void oracle_shared_row_scaled(int H, int Is, const uint16_t* act, double scale, const uint16_t* ws13,
+                              const uint16_t* ws2, double* s_out) {
   double* a = (double*)malloc(sizeof(double) * (size_t)Is);
   for (int i = 0; i < Is; i++) {
     double g = 0.0, u = 0.0;
     for (int j = 0; j < H; j++) {
-      double v = bfd(xn, j);
+      double v = bfd(act, j);
       g += bfd(ws13, (size_t)i * H + j) * v;
       u += bfd(ws13, (size_t)(Is + i) * H + j) * v;
     }
+    g *= scale;
+    u *= scale;
     a[i] = g * sigmoid(g) * u;
   }
   for (int h = 0; h < H; h++) {
@@ -273,6 +286,17 @@ void oracle_shared_row(int H, int Is, const uint16_t* xn, const uint16_t* ws13, 
     s_out[h] = acc;
   }
   free(a);
+}
+
+void oracle_shared_row(int H, int Is, const uint16_t* xn, const uint16_t* ws13, const uint16_t* ws2,
+                       double* s_out) {
+  oracle_shared_row_scaled(H, Is, xn, 1.0, ws13, ws2, s_out);
+}
+
+/* bf16(h * gamma): the norm's input to the projections when rstd is folded
+ * into their sums. */
+static void folded_act(int H, const uint16_t* h, const uint16_t* gamma, uint16_t* hg) {
+  for (int i = 0; i < H; i++) hg[i] = oracle_bf16_round(bfd(h, i) * bfd(gamma, i));
 }
 
 /* The shared expert's gate: sigmoid(wg . xn), the dot product in double. */
@@ -287,7 +311,7 @@ double oracle_shared_gate(int H, const uint16_t* xn, const uint16_t* wg) {
  * [rows, E]; ids, w: [rows, K]; y_routed, y_shared: [rows, H].  sgate [H]
  * may be NULL (no shared gate); y_shared is the gated shared output. */
 int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, double eps, int n_group,
-                    int topk_group, double routed_scale, int wfmt,
+                    int topk_group, double routed_scale, int wfmt, int fold,
                     const uint16_t* x, const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w,
                     const float* bias, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                     const uint8_t* w2_s, const uint16_t* ws13, const uint16_t* ws2, const uint16_t* sgate,
@@ -301,6 +325,7 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
     return 1;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  uint16_t* hg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   double* lg = (double*)malloc(sizeof(double) * (size_t)E);
   double* ky = (double*)malloc(sizeof(double) * (size_t)E);
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
@@ -312,8 +337,15 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
   const size_t e2 = (size_t)H * (wfmt == 1 ? I : I / 2), e2s = (size_t)H * (I / 32);
   for (int row = 0; row < rows; row++) {
     const size_t ro = (size_t)row * H;
-    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
-    oracle_router_row(H, E, xn, router_w, lg);
+    double rstd;
+    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, &rstd);
+    if (fold) {
+      folded_act(H, h, gamma, hg);
+      oracle_router_row(H, E, hg, router_w, lg);
+      for (int e = 0; e < E; e++) lg[e] *= rstd;
+    } else {
+      oracle_router_row(H, E, xn, router_w, lg);
+    }
     oracle_keys(E, scoring, lg, bias, ky);
     oracle_topk_grouped(E, K, ky, n_group, topk_group, ids);
     oracle_topk_weights(K, scoring, lg, ids, w);
@@ -325,7 +357,7 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
       for (int j = 0; j < H; j++) yr[j] += w[k] * d[j];
     }
     for (int j = 0; j < H; j++) ys[j] = 0.0;
-    if (Is > 0) oracle_shared_row(H, Is, xn, ws13, ws2, ys);
+    if (Is > 0) oracle_shared_row_scaled(H, Is, fold ? hg : xn, fold ? rstd : 1.0, ws13, ws2, ys);
     if (Is > 0 && sgate) {
       const double sg = oracle_shared_gate(H, xn, sgate);
       for (int j = 0; j < H; j++) ys[j] *= sg;
@@ -340,22 +372,31 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
     if (y_routed_out) memcpy(y_routed_out + ro, yr, sizeof(double) * (size_t)H);
     if (y_shared_out) memcpy(y_shared_out + ro, ys, sizeof(double) * (size_t)H);
   }
-  free(h); free(xn); free(lg); free(ky); free(ids); free(w); free(d); free(yr); free(ys);
+  free(h); free(xn); free(hg); free(lg); free(ky); free(ids); free(w); free(d); free(yr); free(ys);
   return 0;
 }
 
 /* Norm + router + keys only (used to check the top-k gap of generated rows). */
-int oracle_router_keys(int rows, int H, int E, int scoring, double eps, const uint16_t* x, const uint16_t* r,
-                       const uint16_t* gamma, const uint16_t* router_w, const float* bias, double* logits_out,
-                       double* keys_out) {
+int oracle_router_keys(int rows, int H, int E, int scoring, double eps, int fold, const uint16_t* x,
+                       const uint16_t* r, const uint16_t* gamma, const uint16_t* router_w, const float* bias,
+                       double* logits_out, double* keys_out) {
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  uint16_t* hg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   for (int row = 0; row < rows; row++) {
     const size_t ro = (size_t)row * H;
-    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, NULL);
-    oracle_router_row(H, E, xn, router_w, logits_out + (size_t)row * E);
-    oracle_keys(E, scoring, logits_out + (size_t)row * E, bias, keys_out + (size_t)row * E);
+    double* lg = logits_out + (size_t)row * E;
+    double rstd;
+    oracle_norm_row(H, eps, x + ro, r ? r + ro : NULL, gamma, h, xn, &rstd);
+    if (fold) {
+      folded_act(H, h, gamma, hg);
+      oracle_router_row(H, E, hg, router_w, lg);
+      for (int e = 0; e < E; e++) lg[e] *= rstd;
+    } else {
+      oracle_router_row(H, E, xn, router_w, lg);
+    }
+    oracle_keys(E, scoring, lg, bias, keys_out + (size_t)row * E);
   }
-  free(h); free(xn);
+  free(h); free(xn); free(hg);
   return 0;
 }

@@ -555,3 +555,82 @@ def test_mxfp8_copy_of_mxfp4_weights_gives_the_same_tail():
     o8 = oracle.moe_tail(x, r, w8, dataclasses.replace(cfg, weight_format=1))
     for k in ("ids", "w", "y_routed", "y_shared", "out"):
         np.testing.assert_array_equal(o8[k], o4[k])
+
+
+# ---- the norm folded into the router and shared projections ------------------------
+
+def _times8(a):
+    """bf16 bit patterns times 8 (exact: only the exponent moves)."""
+    return (a + np.uint16(3 << 7) * ((a & 0x7F80) != 0)).astype(np.uint16)
+
+
+def test_folded_norm_with_unit_gamma_is_rstd_times_the_raw_projection():
+    """With gamma = 1, bf16(h * gamma) = h exactly, so the folded logits are
+    rstd * (h . Wr) and the shared expert's gate/up sums are rstd * (Ws13 . h)
+    (the pages' fold of the router norm into its logits and into the next
+    projections' activation scales).  x is scaled by 8 so that rstd is far
+    from 1 and a missing or inverted rstd is visible."""
+    import dataclasses
+
+    cfg = dataclasses.replace(synth.CONFIGS["c0"].with_rows(2), fold_norm=1)
+    w = dict(synth.make_weights(cfg))
+    w["gamma"] = np.full(cfg.hidden, 0x3F80, np.uint16)
+    x, r = synth.make_rows(cfg)
+    x = _times8(x)
+    o = oracle.moe_tail(x, r, w, cfg)
+    Wr = synth.bf16_bits_to_f32(w["router_w"]).astype(np.float64)
+    W13 = synth.bf16_bits_to_f32(w["ws13"]).astype(np.float64)
+    W2 = synth.bf16_bits_to_f32(w["ws2"]).astype(np.float64)
+    Is = cfg.shared_inter
+    for row in range(cfg.rows):
+        h, xn, rstd = oracle.norm_row(x[row], r[row], w["gamma"], cfg.eps)
+        assert rstd < 0.25
+        hv = synth.bf16_bits_to_f32(h).astype(np.float64)
+        np.testing.assert_allclose(o["logits"][row], rstd * (Wr @ hv), rtol=1e-12, atol=1e-14)
+        g, u = rstd * (W13[:Is] @ hv), rstd * (W13[Is:] @ hv)
+        np.testing.assert_allclose(o["y_shared"][row], W2 @ (g / (1 + np.exp(-g)) * u), rtol=1e-10, atol=1e-14)
+        np.testing.assert_array_equal(o["xn"][row], xn)  # the normed row itself is unchanged
+
+
+def test_folded_logits_stay_within_two_bf16_roundings_of_the_plain_ones():
+    """Folded and plain logits project the same real vector h*rstd*gamma, one
+    through bf16(h*gamma) then times rstd, the other through bf16(h*rstd*gamma):
+    each rounding is at most 2^-9 relative per element, so the logits differ by
+    at most rstd * sum_i |Wr_ei h_i gamma_i| * 2^-8 -- and they do differ."""
+    import dataclasses
+
+    cfg = synth.CONFIGS["c3"].with_rows(2)
+    w = synth.make_router_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    x = _times8(x)
+    lp, _ = oracle.router_keys(x, r, w, cfg)
+    lf, _ = oracle.router_keys(x, r, w, dataclasses.replace(cfg, fold_norm=1))
+    Wr = np.abs(synth.bf16_bits_to_f32(w["router_w"]).astype(np.float64))
+    gm = synth.bf16_bits_to_f32(w["gamma"]).astype(np.float64)
+    for row in range(cfg.rows):
+        h, _, rstd = oracle.norm_row(x[row], r[row], w["gamma"], cfg.eps)
+        hv = np.abs(synth.bf16_bits_to_f32(h).astype(np.float64) * gm)
+        bound = rstd * (Wr @ hv) * 2.0**-8 * (1 + 1e-9)
+        d = np.abs(lf[row] - lp[row])
+        assert np.all(d <= bound)
+        assert np.count_nonzero(d) > cfg.experts // 2
+
+
+def test_folded_norm_leaves_the_routed_experts_on_xn():
+    """With one pick (weight exactly 1) and the same expert chosen, the routed
+    output is the same bit for bit with or without the fold: the routed
+    experts project xn either way."""
+    import dataclasses
+
+    cfg = dataclasses.replace(synth.CONFIGS["c0"].with_rows(4), topk=1)
+    w = synth.make_weights(cfg)
+    x, r = synth.make_rows(cfg)
+    o = oracle.moe_tail(x, r, w, cfg)
+    of = oracle.moe_tail(x, r, w, dataclasses.replace(cfg, fold_norm=1))
+    same = (o["ids"] == of["ids"]).ravel()
+    assert same.sum() >= 3
+    np.testing.assert_array_equal(of["w"], 1.0)
+    np.testing.assert_array_equal(of["y_routed"][same], o["y_routed"][same])
+    np.testing.assert_array_equal(of["xn"], o["xn"])
+    np.testing.assert_array_equal(of["h"], o["h"])
+    assert not np.array_equal(of["y_shared"], o["y_shared"])
