@@ -110,7 +110,7 @@ class Workload:
         self.res_out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
         self.ids = torch.empty((rows, cfg.topk), dtype=torch.int32, device="cuda")
         c = binding.make_config(rows, H, cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter, cfg.scoring, cfg.eps,
-                                weight_format=cfg.weight_format)
+                                weight_format=cfg.weight_format, fold_norm=cfg.fold_norm)
         self.h = binding.MoeTail(c)
         self.rows = rows
 
@@ -241,6 +241,7 @@ def main():
     ap.add_argument("--only", default=None, help="time one workload only, e.g. c2 or c1:4")
     ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
     ap.add_argument("--fp8", action="store_true", help="with --only: MXFP8 (E4M3) routed experts")
+    ap.add_argument("--fold", action="store_true", help="with --only: the norm folded into the router/shared sums")
     ap.add_argument("--calib", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -261,8 +262,8 @@ def main():
         print(json.dumps({"calib_copy_bytes": a.numel(), "copies": 10}))
         return
 
-    def measure(name, rows, fmt=0):
-        cfg = dataclasses.replace(cfgs[name], weight_format=fmt)
+    def measure(name, rows, fmt=0, fold=0):
+        cfg = dataclasses.replace(cfgs[name], weight_format=fmt, fold_norm=fold)
         guess = {1: 10, 2: 20, 4: 39, 8: 56, 16: 139}.get(rows, rows * cfg.topk)
         L = copies_for(cfg, rows, guess)
         wl = Workload(cfg, rows, L, torch)
@@ -270,7 +271,7 @@ def main():
         dist = wl.distinct(s)
         us = wl.time_eager(args.steps, args.warmup) if args.eager else wl.time(args.steps, args.warmup)
         B = alg_bytes(cfg, rows, dist)
-        rec = {"workload": name + ("-mxfp8" if fmt else ""), "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
+        rec = {"workload": name + ("-mxfp8" if fmt else "") + ("-fold" if fold else ""), "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
                "us_per_call": round(us, 3), "GBps": round(B / (us * 1e-6) / 1e9, 1),
                "frac_of_peak": round(B / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
         print(json.dumps(rec), file=sys.stderr, flush=True)
@@ -280,7 +281,7 @@ def main():
 
     if args.only:
         name, _, rows = args.only.partition(":")
-        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0)
+        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0)
         return
 
     head = measure("c2", 8)
@@ -292,6 +293,8 @@ def main():
         sweep.append(measure("c3", 4))
         sweep.append(measure("c4", 16))
         sweep.append(measure("c2", 8, 1))
+        sweep.append(measure("c2", 8, 0, 1))
+        sweep.append(measure("c1", 1, 0, 1))
     copy_gbps = copy_bandwidth(torch)
     cpu = cpu_baseline(cfgs["c2"]) if args.cpu else None
     us = head["us_per_call"]

@@ -113,6 +113,7 @@ struct Params {
   int R, H, E, K, I, Is, scoring, G;
   int n_group, topk_group;  // group-limited routing (n_group 1: none)
   int f8;                   // routed experts in MXFP8 (E4M3 codes), else MXFP4
+  int fold;                 // rstd multiplies the router and shared gate/up sums over bf16(h * gamma)
   float rscale;             // routed scaling factor
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
   int rsum;                       // top-k readers sum the router K-chunk partials themselves
@@ -152,6 +153,7 @@ struct Params {
   uint64_t* lgt;    // [R][Ep] tagged fp32 logits
   uint64_t* part1;  // [blocks * S1][16][16] tagged fp32 K-chunk partial sums
   uint64_t* gpart;  // [R][NQ] tagged fp32 partial dots of the shared gate, one per norm slice
+  uint64_t* rstdt;  // [R] tagged fp32 rstd of each row (folded norm)
   uint16_t* a_s;
   uint16_t* a_r;
 };
@@ -486,6 +488,7 @@ struct Shared {
   uint32_t ep;
   double tmpd[NW];
   float tmpg[NW];             // shared gate: each wave's partial dot of a norm slice
+  float rstd[MAX_R];          // folded norm: each row's rstd
   float gsum[MAX_R * NQ];     // shared gate: the slices' partial dots, per row
   float sgw[MAX_R];           // shared gate: sigmoid(wg . xn) per row
   int wcnt[NW];
@@ -648,11 +651,13 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         nv[c] = n0 | (n1 << 16);
       }
       stc16(rs_xn, (uint32_t)(row * H + i) * 2u, nv);
+      if (!(FEAT && p.fold))
 #pragma unroll
-      for (int c = 0; c < 4; ++c) st_tag(p.xnt + (size_t)(row * H + i) / 2 + c, nv[c], epn);
+        for (int c = 0; c < 4; ++c) st_tag(p.xnt + (size_t)(row * H + i) / 2 + c, nv[c], epn);
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
       nvs = nv;
     }
+    if (FEAT && p.fold && q == 0 && tid == 0) st_tag(p.rstdt + row, __float_as_uint((float)rstd), epn);
     if (FEAT && p.sgate) {  // this slice's share of the gate's dot product: lanes, waves in order
       float gd = 0.f;
       if (sl) {
@@ -711,7 +716,30 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 
   // ---- router/shared phase: stage this chunk of xn (tagged words written by
   // the norm workgroups), then the items' MFMA tiles
-  if (nu1) {
+  if (nu1 && FEAT && p.fold) {
+    // folded norm: this chunk of bf16(h * gamma), from the inputs themselves
+    // (no wait for the norm workgroups; rstd is applied to the sums)
+    const int CW = TC * 32, c8n = CW / 8, n8 = R * c8n;
+    const rsrc_t rx = make_rsrc(p.x, (uint32_t)(R * H * 2));
+    const rsrc_t rr = make_rsrc(p.res ? p.res : p.x, p.res ? (uint32_t)(R * H * 2) : 0u);
+    const rsrc_t rg = make_rsrc(p.gamma, (uint32_t)(H * 2));
+    for (int w = tid; w < n8; w += NT) {
+      const int r = w / c8n, c8 = w - r * c8n, col = s1 * CW + c8 * 8;
+      const u32x4 xv = ld16<0>(rx, (uint32_t)(r * H + col) * 2u);
+      const u32x4 rv = ld16<0>(rr, (uint32_t)(r * H + col) * 2u);
+      const u32x4 gv = ld16<0>(rg, (uint32_t)col * 2u);
+      u32x4 hg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t h0 = f2bf(bf2f(xv[c] & 0xFFFFu) + bf2f(rv[c] & 0xFFFFu));
+        const uint32_t h1 = f2bf(bf2f(xv[c] >> 16) + bf2f(rv[c] >> 16));
+        hg[c] = f2bf(bf2f(h0) * bf2f(gv[c] & 0xFFFFu)) | (f2bf(bf2f(h1) * bf2f(gv[c] >> 16)) << 16);
+      }
+      *(u32x4*)(xc + r * p.cs + c8 * 8) = hg;
+    }
+    for (int c = tid * 8; c < p.cs; c += NT * 8) *(u32x4*)(xc + xzero * p.cs + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  } else if (nu1) {
     const int CW = TC * 32, pr = CW / 4, np2 = R * pr;  // word pairs per row, in all
     if (!poll_all([&]() {
           bool ok = true;
@@ -764,6 +792,15 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     S.last[tid] = old == (uint32_t)(S1 - 1);
   }
   __syncthreads();
+  if (FEAT && p.fold) {  // every row's rstd (tagged words of the norm workgroups)
+    if (!poll_all([&]() {
+          if (tid >= R) return true;
+          const uint64_t v = ld_tag(p.rstdt + tid);
+          S.rstd[tid] = __uint_as_float((uint32_t)v);
+          return tag_ok(v, ep);
+        }, 0, 2, stall))
+      return;
+  }
   {
     int nr = 0;
     for (int k = 0; k < nu1; ++k) {  // router blocks: logits = sum of the chunks in chunk order
@@ -779,6 +816,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
         for (int s = 0; s < NQ; ++s)
           if (s < S1) v += t[s];
+        if (FEAT && p.fold) v *= S.rstd[col];
         const int e = u * 16 + row;
         if (e < E) st_tag(p.lgt + col * p.Ep + e, __float_as_uint(v), ep);
       }
@@ -814,6 +852,10 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           gs += tg[s];
           us += tu[s];
         }
+      if (FEAT && p.fold) {
+        gs *= S.rstd[col];
+        us *= S.rstd[col];
+      }
       const float a = gs / (1.f + __expf(-gs)) * us;
       stc2(rs_as, (uint32_t)(col * Is + sb * 8 + row) * 2u, f2bf(a));
     }
@@ -873,9 +915,10 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
                   ok = ok && t[s][j >> 1][2 * (j & 1) + 1] == ep;
                   v[j] += __uint_as_float(t[s][j >> 1][2 * (j & 1)]);
                 }
+            const float sc = FEAT && p.fold ? S.rstd[r] : 1.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (e + j < E) lgs[r * E + e + j] = v[j];
+              if (e + j < E) lgs[r * E + e + j] = v[j] * sc;
           }
           return ok;
         }, 1, 0, false))
@@ -1468,7 +1511,7 @@ static const void* kernel_for(const Params& p) {
     if (!p.xn_lds) return (const void*)moe_tail_kernel_gm_f8;
     return p.rsum ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_f8;
   }
-  const bool f = p.sgate || p.n_group > 1;
+  const bool f = p.sgate || p.n_group > 1 || p.fold;
   if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f : (const void*)moe_tail_kernel_gm;
   if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f : (const void*)moe_tail_kernel_lds_rs;
   return f ? (const void*)moe_tail_kernel_lds_f : (const void*)moe_tail_kernel_lds;
@@ -1532,6 +1575,7 @@ struct moe_tail {
   uint64_t* lgt;
   uint64_t* part1;
   uint64_t* gpart;
+  uint64_t* rstdt;
   size_t scratch_bytes;
   uint16_t* a_s;
   uint16_t* a_r;
@@ -1575,6 +1619,8 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
                          c->top_k > c->topk_group * (c->num_experts / c->n_group)))
     return fail(nullptr, MOE_TAIL_EINVAL, "topk_group %d must be in 1..n_group and keep at least top_k experts",
                 c->topk_group);
+  if (c->fold_norm != 0 && c->fold_norm != 1)
+    return fail(nullptr, MOE_TAIL_EINVAL, "fold_norm %d must be 0 or 1", c->fold_norm);
   if (c->weight_format != MOE_TAIL_MXFP4 && c->weight_format != MOE_TAIL_MXFP8)
     return fail(nullptr, MOE_TAIL_EINVAL, "unknown weight_format %d", c->weight_format);
   if (!(c->routed_scale >= 0.f) || !isfinite(c->routed_scale))
@@ -1641,7 +1687,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
   const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_xnt = o_xn + al(R * H * 2);
   const size_t o_lg = o_xnt + al(R * H * 4), o_pt = o_lg + al(R * (size_t)h->Ep * 8);
-  const size_t o_gp = o_pt + al((size_t)n_it * 2048), o_as = o_gp + al(R * mt::NQ * 8);
+  const size_t o_gp = o_pt + al((size_t)n_it * 2048), o_rs = o_gp + al(R * mt::NQ * 8), o_as = o_rs + al(R * 8);
   const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
   (void)E;
   int prev = 0;
@@ -1677,6 +1723,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->lgt = (uint64_t*)(base + o_lg);
   h->part1 = (uint64_t*)(base + o_pt);
   h->gpart = (uint64_t*)(base + o_gp);
+  h->rstdt = (uint64_t*)(base + o_rs);
   h->scratch_bytes = total;
   h->a_s = (uint16_t*)(base + o_as);
   h->a_r = (uint16_t*)(base + o_ar);
@@ -1725,6 +1772,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.topk_group = c.n_group > 1 ? c.topk_group : 1;
   p.rscale = c.routed_scale > 0.f ? c.routed_scale : 1.f;
   p.f8 = c.weight_format == MOE_TAIL_MXFP8;
+  p.fold = c.fold_norm;
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
   // reader-side router sums when each thread then loads at most 8 partials
@@ -1777,6 +1825,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   p.lgt = h->lgt;
   p.part1 = h->part1;
   p.gpart = h->gpart;
+  p.rstdt = h->rstdt;
   p.a_s = h->a_s;
   p.a_r = h->a_r;
 

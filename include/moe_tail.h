@@ -88,6 +88,11 @@ typedef struct {
   int32_t topk_group;   /* groups kept, 1..n_group, with K <= topk_group * E / n_group */
   float routed_scale;   /* routed scaling factor on the top-k weights; 0 means 1 */
   int32_t weight_format; /* routed expert codes: MOE_TAIL_MXFP4 (0) or MOE_TAIL_MXFP8 (1) */
+  int32_t fold_norm;     /* 1: the norm is folded into the router and shared gate/up sums: they project
+                            bf16(h * gamma) and are multiplied by the row's rstd afterwards ("glm53:
+                            Long-context indexer ...", PR 85 commit text: the router's norm moves into its
+                            logits; not bitwise equal to projecting xn).  The routed experts and the shared
+                            gate still take xn.  0: plain (the router and shared expert project xn) */
 } moe_tail_config;
 
 typedef struct {

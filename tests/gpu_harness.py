@@ -32,7 +32,8 @@ def device_weights(name: str):
 def handle_for(cfg, max_rows=None, **kw):
     c = binding.make_config(max_rows or cfg.rows, cfg.hidden, cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter,
                             cfg.scoring, cfg.eps, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                            routed_scale=cfg.routed_scale, weight_format=cfg.weight_format, **kw)
+                            routed_scale=cfg.routed_scale, weight_format=cfg.weight_format,
+                            fold_norm=cfg.fold_norm, **kw)
     return binding.MoeTail(c)
 
 

@@ -26,8 +26,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # moe_tail_config: 14 x 4-byte integer fields + 2 floats; moe_tail_args: 19 pointers
-    assert ctypes.sizeof(binding.Config) == 16 * 4
+    # moe_tail_config: 15 x 4-byte integer fields + 2 floats; moe_tail_args: 19 pointers
+    assert ctypes.sizeof(binding.Config) == 17 * 4
     assert ctypes.sizeof(binding.Args) == 19 * 8
 
 
@@ -49,7 +49,7 @@ def test_check_config_accepts_the_workloads():
     ("debug_flags", 4), ("debug_flags", 6),
     ("n_group", 3), ("n_group", 128), ("n_group", -1),
     ("routed_scale", -1.0), ("routed_scale", float("inf")),
-    ("weight_format", 2), ("weight_format", -1),
+    ("weight_format", 2), ("weight_format", -1), ("fold_norm", 2), ("fold_norm", -1),
 ])
 def test_check_config_refusals(field, value):
     c = good()
@@ -78,6 +78,7 @@ def test_both_weight_formats_accepted():
     for fmt in (binding.MXFP4, binding.MXFP8):
         c = good()
         c.weight_format = fmt
+        c.fold_norm = 1
         assert binding.check_config(c) == binding.OK, fmt
 
 

@@ -190,3 +190,26 @@ def test_mxfp8_matches_mxfp4_on_reencoded_weights(name, rows):
     assert h8.get_error() == 0
     for k in ("ids", "w", "logits", "y_routed", "y_shared", "out", "res_out"):
         np.testing.assert_array_equal(g8[k], g4[k], err_msg=k)
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 1), ("c1", 1), ("c1", 8), ("c3", 4), ("c4", 16)])
+def test_parity_folded_norm(name, rows):
+    """The norm folded into the router and shared gate/up sums (rstd applied
+    after projecting bf16(h * gamma); "glm53: Long-context indexer ...", PR 85
+    commit text) against the oracle's folded form, on every kernel path:
+    routed sums by every reader (c0, c1 at 1 row), xn in LDS (c1 at 8 rows,
+    c3 with sigmoid keys), xn from global scratch (c4 at 16 rows).  Rows are
+    gap-checked on the folded keys."""
+    import dataclasses
+
+    cfg = dataclasses.replace(synth.CONFIGS[name].with_rows(rows), fold_norm=1)
+    _say("fold", name, rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    h = handle_for(cfg)
+    g = run(h, cfg, device_weights(name), x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    plain = oracle.moe_tail(x, r, w, synth.CONFIGS[name].with_rows(rows))
+    assert not np.array_equal(plain["logits"], o["logits"])  # the fold changed the logits
