@@ -594,8 +594,34 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     return f;
   };
   const bool is_norm = cta < R * NQ;
+  // Folded norm: this workgroup's K chunk of x, r and gamma (the first FCH
+  // 16-byte vectors of each per thread) is loaded ahead of the weights, so
+  // that it does not queue behind them; every load is issued (out-of-range
+  // offsets where not needed) to keep the wait counts static.
+  constexpr int FCH = 2;
+  const bool fold = FEAT && p.fold && nu1;
+  const int fc8n = TC * 4, fn8 = R * fc8n;  // 8-element vectors per chunk row, in all
+  const rsrc_t frx = make_rsrc(p.x, (uint32_t)(R * H * 2));
+  const rsrc_t frr = make_rsrc(p.res ? p.res : p.x, p.res ? (uint32_t)(R * H * 2) : 0u);
+  const rsrc_t frg = make_rsrc(p.gamma, (uint32_t)(H * 2));
+  u32x4 fx[FCH], fr[FCH], fg[FCH];
+  auto fold_load = [&](int w, u32x4& xv, u32x4& rv, u32x4& gv) {
+    const bool v = fold && w < fn8;
+    const int r = w / fc8n, col = s1 * TC * 32 + (w - r * fc8n) * 8;
+    xv = ld16<0>(frx, v ? (uint32_t)(r * H + col) * 2u : OOB);
+    rv = ld16<0>(frr, v ? (uint32_t)(r * H + col) * 2u : OOB);
+    gv = ld16<0>(frg, v ? (uint32_t)col * 2u : OOB);
+  };
+  auto fold_issue = [&]() {
+    if constexpr (FEAT) {
+      if (fold)
+#pragma unroll
+        for (int k = 0; k < FCH; ++k) fold_load(tid + k * NT, fx[k], fr[k], fg[k]);
+    }
+  };
   // weights do not depend on the activations: their loads go out first,
   // except in the norm workgroups, whose row loads must not queue behind them
+  fold_issue();
   if (!is_norm) w1.prime(p1_next);
 
   // ---- P0: fused residual add + RMSNorm; workgroup c < R*NQ owns slice c % NQ of row c / NQ
@@ -677,6 +703,31 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       }
     }
   }
+  if (FEAT && fold) {
+    // folded norm: this chunk of bf16(h * gamma), from the inputs themselves
+    // (no wait for the norm workgroups or the epoch; rstd is applied to the sums)
+    auto put = [&](int w, const u32x4& xv, const u32x4& rv, const u32x4& gv) {
+      if (w >= fn8) return;
+      const int r = w / fc8n, c8 = w - r * fc8n;
+      u32x4 hg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t h0 = f2bf(bf2f(xv[c] & 0xFFFFu) + bf2f(rv[c] & 0xFFFFu));
+        const uint32_t h1 = f2bf(bf2f(xv[c] >> 16) + bf2f(rv[c] >> 16));
+        hg[c] = f2bf(bf2f(h0) * bf2f(gv[c] & 0xFFFFu)) | (f2bf(bf2f(h1) * bf2f(gv[c] >> 16)) << 16);
+      }
+      *(u32x4*)(xc + r * p.cs + c8 * 8) = hg;
+    };
+#pragma unroll
+    for (int k = 0; k < FCH; ++k) put(tid + k * NT, fx[k], fr[k], fg[k]);
+    for (int w = tid + FCH * NT; w < fn8; w += NT) {  // chunks beyond FCH vectors per thread
+      u32x4 xv, rv, gv;
+      fold_load(w, xv, rv, gv);
+      put(w, xv, rv, gv);
+    }
+    for (int c = tid * 8; c < p.cs; c += NT * 8) *(u32x4*)(xc + xzero * p.cs + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   if (tid == 0) {
     uint32_t e1 = epv;
     asm volatile("" : "+v"(e1));  // keeps the wait for the atomic's return here
@@ -716,30 +767,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 
   // ---- router/shared phase: stage this chunk of xn (tagged words written by
   // the norm workgroups), then the items' MFMA tiles
-  if (nu1 && FEAT && p.fold) {
-    // folded norm: this chunk of bf16(h * gamma), from the inputs themselves
-    // (no wait for the norm workgroups; rstd is applied to the sums)
-    const int CW = TC * 32, c8n = CW / 8, n8 = R * c8n;
-    const rsrc_t rx = make_rsrc(p.x, (uint32_t)(R * H * 2));
-    const rsrc_t rr = make_rsrc(p.res ? p.res : p.x, p.res ? (uint32_t)(R * H * 2) : 0u);
-    const rsrc_t rg = make_rsrc(p.gamma, (uint32_t)(H * 2));
-    for (int w = tid; w < n8; w += NT) {
-      const int r = w / c8n, c8 = w - r * c8n, col = s1 * CW + c8 * 8;
-      const u32x4 xv = ld16<0>(rx, (uint32_t)(r * H + col) * 2u);
-      const u32x4 rv = ld16<0>(rr, (uint32_t)(r * H + col) * 2u);
-      const u32x4 gv = ld16<0>(rg, (uint32_t)col * 2u);
-      u32x4 hg;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t h0 = f2bf(bf2f(xv[c] & 0xFFFFu) + bf2f(rv[c] & 0xFFFFu));
-        const uint32_t h1 = f2bf(bf2f(xv[c] >> 16) + bf2f(rv[c] >> 16));
-        hg[c] = f2bf(bf2f(h0) * bf2f(gv[c] & 0xFFFFu)) | (f2bf(bf2f(h1) * bf2f(gv[c] >> 16)) << 16);
-      }
-      *(u32x4*)(xc + r * p.cs + c8 * 8) = hg;
-    }
-    for (int c = tid * 8; c < p.cs; c += NT * 8) *(u32x4*)(xc + xzero * p.cs + c) = (u32x4){0u, 0u, 0u, 0u};
-    __syncthreads();
-  } else if (nu1) {
+  if (!(FEAT && fold) && nu1) {
     const int CW = TC * 32, pr = CW / 4, np2 = R * pr;  // word pairs per row, in all
     if (!poll_all([&]() {
           bool ok = true;
@@ -783,6 +811,15 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       }
     });
   }
+  if (FEAT && p.fold) {  // every row's rstd (tagged words of the norm workgroups), while the partials drain
+    if (!poll_all([&]() {
+          if (tid >= R) return true;
+          const uint64_t v = ld_tag(p.rstdt + tid);
+          S.rstd[tid] = __uint_as_float((uint32_t)v);
+          return tag_ok(v, ep);
+        }, 0, 2, stall))
+      return;
+  }
   // count this workgroup's chunk arrivals; the last of a block's S1 chunks sums them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -792,15 +829,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     S.last[tid] = old == (uint32_t)(S1 - 1);
   }
   __syncthreads();
-  if (FEAT && p.fold) {  // every row's rstd (tagged words of the norm workgroups)
-    if (!poll_all([&]() {
-          if (tid >= R) return true;
-          const uint64_t v = ld_tag(p.rstdt + tid);
-          S.rstd[tid] = __uint_as_float((uint32_t)v);
-          return tag_ok(v, ep);
-        }, 0, 2, stall))
-      return;
-  }
   {
     int nr = 0;
     for (int k = 0; k < nu1; ++k) {  // router blocks: logits = sum of the chunks in chunk order
