@@ -213,3 +213,31 @@ def test_parity_folded_norm(name, rows):
     check_against_oracle(g, o, cfg)
     plain = oracle.moe_tail(x, r, w, synth.CONFIGS[name].with_rows(rows))
     assert not np.array_equal(plain["logits"], o["logits"])  # the fold changed the logits
+
+
+@pytest.mark.parametrize("name,rows,n_group,topk_group", [("c3", 4, 8, 4), ("c1", 8, 8, 3)])
+def test_parity_every_option_together(name, rows, n_group, topk_group):
+    """MXFP8 experts, the folded norm, group-limited routing with a routed
+    scale of 2.5 and a shared gate in one call, against the oracle: the
+    optional steps compose (c3: sigmoid keys with a bias, xn in LDS; c1 at 8
+    rows: softmax keys)."""
+    import dataclasses
+
+    from gpu_harness import dev
+
+    cfg = dataclasses.replace(synth.CONFIGS[name].with_rows(rows), weight_format=1, fold_norm=1, n_group=n_group,
+                              topk_group=topk_group, routed_scale=2.5)
+    _say("all options", name, rows, n_group, topk_group)
+    w = dict(synth.make_weights(cfg))
+    w["shared_gate"] = synth.make_shared_gate(cfg)
+    x, r = _grouped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    dw = {k: dev(v) for k, v in w.items()}
+    h = handle_for(cfg)
+    g = run(h, cfg, dw, x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    gs = cfg.experts // n_group
+    for row in range(rows):
+        assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
+    del dw, h
