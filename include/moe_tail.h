@@ -68,7 +68,8 @@ typedef enum { MOE_TAIL_MXFP4 = 0, MOE_TAIL_MXFP8 = 1 } moe_tail_weight_format;
 
 typedef struct {
   int32_t max_rows;     /* largest `rows` any run will pass: 1..16 */
-  int32_t hidden;       /* H: multiple of 128, 128..16384 */
+  int32_t hidden;       /* H: multiple of 128, 128..16384; moe_tail_create also refuses (EUNSUPPORTED) more than
+                           32 hidden rows per compute unit, i.e. H > 8192 on a 256-CU device */
   int32_t num_experts;  /* E: 1..512 */
   int32_t top_k;        /* K: 1..min(E, 32) */
   int32_t inter;        /* I, per-rank expert intermediate: multiple of 32, 32..4096 */
