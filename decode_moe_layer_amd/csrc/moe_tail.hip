@@ -1529,17 +1529,21 @@ MT_KERNEL(moe_tail_kernel_gm, false, false, false, false)
 MT_KERNEL(moe_tail_kernel_lds_f, true, false, true, false)
 MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true, false)
 MT_KERNEL(moe_tail_kernel_gm_f, false, false, true, false)
-// MXFP8 experts (E4M3 codes), with the optional steps
+// MXFP8 experts (E4M3 codes), without and with the optional steps
+MT_KERNEL(moe_tail_kernel_lds_8, true, false, false, true)
+MT_KERNEL(moe_tail_kernel_lds_rs_8, true, true, false, true)
+MT_KERNEL(moe_tail_kernel_gm_8, false, false, false, true)
 MT_KERNEL(moe_tail_kernel_lds_f8, true, false, true, true)
 MT_KERNEL(moe_tail_kernel_lds_rs_f8, true, true, true, true)
 MT_KERNEL(moe_tail_kernel_gm_f8, false, false, true, true)
 #undef MT_KERNEL
 static const void* kernel_for(const Params& p) {
-  if (p.f8) {
-    if (!p.xn_lds) return (const void*)moe_tail_kernel_gm_f8;
-    return p.rsum ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_f8;
-  }
   const bool f = p.sgate || p.n_group > 1 || p.fold;
+  if (p.f8) {
+    if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f8 : (const void*)moe_tail_kernel_gm_8;
+    if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_rs_8;
+    return f ? (const void*)moe_tail_kernel_lds_f8 : (const void*)moe_tail_kernel_lds_8;
+  }
   if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f : (const void*)moe_tail_kernel_gm;
   if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f : (const void*)moe_tail_kernel_lds_rs;
   return f ? (const void*)moe_tail_kernel_lds_f : (const void*)moe_tail_kernel_lds;
@@ -1731,10 +1735,11 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   {
     const void* ks[] = {(const void*)mt::moe_tail_kernel_lds,     (const void*)mt::moe_tail_kernel_lds_rs,
                         (const void*)mt::moe_tail_kernel_lds_f,   (const void*)mt::moe_tail_kernel_lds_rs_f,
+                        (const void*)mt::moe_tail_kernel_lds_8,   (const void*)mt::moe_tail_kernel_lds_rs_8,
                         (const void*)mt::moe_tail_kernel_lds_f8,  (const void*)mt::moe_tail_kernel_lds_rs_f8,
                         (const void*)mt::moe_tail_kernel_gm,      (const void*)mt::moe_tail_kernel_gm_f,
-                        (const void*)mt::moe_tail_kernel_gm_f8};
-    for (int k = plan.xn_lds ? 0 : 6; k < (plan.xn_lds ? 6 : 9) && e == hipSuccess; ++k)
+                        (const void*)mt::moe_tail_kernel_gm_8,    (const void*)mt::moe_tail_kernel_gm_f8};
+    for (int k = plan.xn_lds ? 0 : 8; k < (plan.xn_lds ? 8 : 12) && e == hipSuccess; ++k)
       e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
