@@ -49,9 +49,10 @@
  *     encodings, blocks of 32 elements (the pages name MXFP4 but do not
  *     define it).
  * Readings where the pages are silent (gamma multiplies plainly, eps inside
- * the square root, gate rows first in W13, low nibble = even element, no
- * routed scaling factor, no shared-expert gate) are listed with the design
- * notes of the repository.
+ * the square root, gate rows first in W13, low nibble = even element; the
+ * routed scaling factor, the shared-expert gate, group-limited routing,
+ * MXFP8 codes and the folded norm as options that are off by default) are
+ * listed with the design notes of the repository.
  */
 #include <math.h>
 #include <stdint.h>

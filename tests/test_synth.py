@@ -75,3 +75,21 @@ def test_similar_rows_repeat_about_30_percent():
     picks = np.concatenate([oracle.topk(ky[i], cfg.topk) for i in range(cfg.rows)])
     frac = 1 - len(set(picks.tolist())) / picks.size
     assert 0.27 <= frac <= 0.33
+
+
+def test_mxfp8_codes_are_never_nan_and_cover_every_other_code():
+    """MXFP8 expert codes are drawn uniformly over the 254 E4M3 codes that are
+    not NaN (0x7F and 0xFF, OCP MX v1.0), in the one-byte-per-element layouts
+    [E, 2I, H] and [E, H, I]; the scales keep the MXFP4 shapes."""
+    import dataclasses
+
+    cfg = dataclasses.replace(synth.CONFIGS["c0"], weight_format=1)
+    w = synth.make_weights(cfg)
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    assert w["w13_q"].shape == (E, 2 * I, H) and w["w2_q"].shape == (E, H, I)
+    assert w["w13_s"].shape == (E, 2 * I, H // 32) and w["w2_s"].shape == (E, H, I // 32)
+    codes = np.concatenate([w["w13_q"].ravel(), w["w2_q"].ravel()])
+    counts = np.bincount(codes, minlength=256)
+    assert counts[0x7F] == 0 and counts[0xFF] == 0
+    assert np.count_nonzero(counts) == 254
+    assert counts.max() < 2 * counts[counts > 0].min()  # roughly uniform
