@@ -295,6 +295,7 @@ def main():
         sweep.append(measure("c2", 8, 1))
         sweep.append(measure("c2", 8, 0, 1))
         sweep.append(measure("c1", 1, 0, 1))
+        sweep.append(measure("c1", 32))
     copy_gbps = copy_bandwidth(torch)
     cpu = cpu_baseline(cfgs["c2"]) if args.cpu else None
     us = head["us_per_call"]

@@ -68,7 +68,8 @@ namespace mt {
 constexpr int NT = 512;      // threads per workgroup
 constexpr int NW = NT / 64;  // waves per workgroup
 constexpr int NQ = 16;       // norm slices per row
-constexpr int MAX_R = 16;
+constexpr int MAX_R = 16;          // rows per launch (MFMA columns)
+constexpr int MAX_ROWS_CALL = 32;  // rows per call: more than MAX_R run as balanced launches
 constexpr int MAX_E = 512;
 constexpr int MAX_K = 32;
 constexpr int MAX_P = MAX_R * MAX_K;  // picks per call
@@ -1613,6 +1614,7 @@ struct moe_tail {
   uint16_t* a_r;
   int S1, TC, n_rb, n_sb, Ep;
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
+  int max_rows_call;  // the caller's max_rows (cfg.max_rows is the per-launch one, at most MAX_R)
   char err[256];
 };
 
@@ -1629,8 +1631,8 @@ static moe_tail_status fail(moe_tail_t* h, moe_tail_status st, const char* fmt, 
 
 extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
   if (!c) return fail(nullptr, MOE_TAIL_EINVAL, "config is NULL");
-  if (c->max_rows < 1 || c->max_rows > mt::MAX_R)
-    return fail(nullptr, MOE_TAIL_EINVAL, "max_rows %d outside 1..%d", c->max_rows, mt::MAX_R);
+  if (c->max_rows < 1 || c->max_rows > mt::MAX_ROWS_CALL)
+    return fail(nullptr, MOE_TAIL_EINVAL, "max_rows %d outside 1..%d", c->max_rows, mt::MAX_ROWS_CALL);
   if (c->hidden < 128 || c->hidden > 16384 || c->hidden % 128)
     return fail(nullptr, MOE_TAIL_EINVAL, "hidden %d must be a multiple of 128 in 128..16384", c->hidden);
   if (c->num_experts < 1 || c->num_experts > mt::MAX_E)
@@ -1673,6 +1675,11 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   *out = nullptr;
   moe_tail_status st = moe_tail_check_config(cfg);
   if (st != MOE_TAIL_OK) return st;
+  // everything below is sized per launch: at most MAX_R rows
+  const int max_rows_call = cfg->max_rows;
+  moe_tail_config icfg = *cfg;
+  if (icfg.max_rows > mt::MAX_R) icfg.max_rows = mt::MAX_R;
+  cfg = &icfg;
   int dev = cfg->device;
   if (dev < 0) HIPCHK(nullptr, hipGetDevice(&dev));
   hipDeviceProp_t prop;
@@ -1702,6 +1709,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   moe_tail_t* h = (moe_tail_t*)calloc(1, sizeof(moe_tail_t));
   if (!h) return fail(nullptr, MOE_TAIL_ENOMEM, "host allocation failed");
   h->cfg = *cfg;
+  h->max_rows_call = max_rows_call;
   h->device = dev;
   h->G = G;
   h->lds_dyn = dyn;
@@ -1767,9 +1775,8 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
-  if (!h) return fail(nullptr, MOE_TAIL_EINVAL, "handle is NULL");
-  if (!a) return fail(h, MOE_TAIL_EINVAL, "args is NULL");
+// One launch over rows <= MAX_R.
+static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
   const moe_tail_config& c = h->cfg;
   if (rows < 1 || rows > c.max_rows) return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, c.max_rows);
   const void* req[] = {a->x, a->gamma, a->router_w, a->w13_q, a->w13_s, a->w2_q, a->w2_s, a->out};
@@ -1874,6 +1881,40 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   else
     e = hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, s);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "kernel launch: %s", hipGetErrorString(e));
+  return MOE_TAIL_OK;
+}
+
+extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
+  if (!h) return fail(nullptr, MOE_TAIL_EINVAL, "handle is NULL");
+  if (!a) return fail(h, MOE_TAIL_EINVAL, "args is NULL");
+  if (rows < 1 || rows > h->max_rows_call)
+    return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, h->max_rows_call);
+  if (rows <= mt::MAX_R) return run_launch(h, rows, a, stream);
+  // More rows than one launch's MFMA columns: balanced row ranges, one
+  // launch each, in order on the stream (each streams its own experts)
+  const int n = (rows + mt::MAX_R - 1) / mt::MAX_R;
+  const size_t H = h->cfg.hidden, E = h->cfg.num_experts, K = h->cfg.top_k;
+  for (int i = 0; i < n; ++i) {
+    const int r0 = i * rows / n, r1 = (i + 1) * rows / n;
+    moe_tail_args b = *a;
+    auto off16 = [&](const void* q, size_t per_row) -> void* {
+      return q ? (void*)((const uint16_t*)q + (size_t)r0 * per_row) : nullptr;
+    };
+    auto off32 = [&](const void* q, size_t per_row) -> void* {
+      return q ? (void*)((const uint32_t*)q + (size_t)r0 * per_row) : nullptr;
+    };
+    b.x = off16(a->x, H);
+    b.residual = off16(a->residual, H);
+    b.out = (uint16_t*)off16(a->out, H);
+    b.res_out = (uint16_t*)off16(a->res_out, H);
+    b.topk_ids = (int32_t*)off32(a->topk_ids, K);
+    b.topk_w = (float*)off32(a->topk_w, K);
+    b.dbg_logits = (float*)off32(a->dbg_logits, E);
+    b.dbg_y_routed = (float*)off32(a->dbg_y_routed, H);
+    b.dbg_y_shared = (float*)off32(a->dbg_y_shared, H);
+    const moe_tail_status st = run_launch(h, r1 - r0, &b, stream);
+    if (st != MOE_TAIL_OK) return st;
+  }
   return MOE_TAIL_OK;
 }
 

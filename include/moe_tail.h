@@ -67,7 +67,7 @@ typedef enum { MOE_TAIL_MXFP4 = 0, MOE_TAIL_MXFP8 = 1 } moe_tail_weight_format;
 #define MOE_TAIL_DEBUG_STALL_ONCE 2u
 
 typedef struct {
-  int32_t max_rows;     /* largest `rows` any run will pass: 1..16 */
+  int32_t max_rows;     /* largest `rows` any run will pass: 1..32 (above 16, see moe_tail_run) */
   int32_t hidden;       /* H: multiple of 128, 128..16384; moe_tail_create also refuses (EUNSUPPORTED) more than
                            32 hidden rows per compute unit, i.e. H > 8192 on a 256-CU device */
   int32_t num_experts;  /* E: 1..512 */
@@ -135,7 +135,10 @@ moe_tail_status moe_tail_check_config(const moe_tail_config* cfg);
 moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
 
 /* Enqueue one call on `stream` (a hipStream_t; NULL = default stream) and
- * return without synchronising.  1 <= rows <= max_rows.  Graph-capturable:
+ * return without synchronising.  1 <= rows <= max_rows.  One launch takes up
+ * to 16 rows (its MFMA columns); more rows (MTP verify batches) run as
+ * ceil(rows / 16) launches over balanced row ranges, in order on the stream,
+ * each de-duplicating and streaming its own experts.  Graph-capturable:
  * the handle's per-call epoch lives in device memory, so replays need no
  * host work.  Calls on one handle must be ordered (one stream at a time).
  * Argument errors are returned synchronously and nothing is enqueued; a

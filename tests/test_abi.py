@@ -43,7 +43,7 @@ def test_check_config_accepts_the_workloads():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("max_rows", 0), ("max_rows", 17), ("hidden", 100), ("hidden", 6000), ("hidden", 32768),
+    ("max_rows", 0), ("max_rows", 33), ("hidden", 100), ("hidden", 6000), ("hidden", 32768),
     ("num_experts", 0), ("num_experts", 513), ("top_k", 0), ("top_k", 33), ("inter", 48), ("inter", 0),
     ("shared_inter", 40), ("shared_inter", -32), ("scoring", 2), ("eps", 0.0), ("eps", float("nan")),
     ("debug_flags", 4), ("debug_flags", 6),
@@ -72,6 +72,11 @@ def test_grouped_routing_accepted_and_refused():
     assert binding.check_config(c) == binding.EINVAL
     c.n_group, c.topk_group, c.routed_scale = 0, 0, 0.0  # zeroed fields: plain routing, scale 1
     assert binding.check_config(c) == binding.OK
+
+
+def test_up_to_32_rows_accepted():
+    for rows in (16, 17, 32):
+        assert binding.check_config(binding.make_config(rows, 6144, 512, 10, 256, 512)) == binding.OK, rows
 
 
 def test_both_weight_formats_accepted():

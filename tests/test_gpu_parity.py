@@ -241,3 +241,24 @@ def test_parity_every_option_together(name, rows, n_group, topk_group):
     for row in range(rows):
         assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
     del dw, h
+
+
+@pytest.mark.parametrize("name,rows,max_rows", [("c1", 32, 32), ("c3", 20, 24), ("c0", 17, 32)])
+def test_parity_above_16_rows(name, rows, max_rows):
+    """More rows than one launch's 16 MFMA columns (MTP verify batches) run as
+    balanced row ranges, one launch each: parity with the oracle on every row,
+    and the first range equals a call on those rows alone, bit for bit."""
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    _say("rows", name, rows, "max_rows", max_rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    h = handle_for(cfg, max_rows=max_rows)
+    g = run(h, cfg, device_weights(name), x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    n = (rows + 15) // 16
+    r1 = rows // n
+    g1 = run(h, cfg.with_rows(r1), device_weights(name), x[:r1], r[:r1])
+    for k in ("ids", "w", "out", "res_out", "y_routed", "y_shared", "logits"):
+        np.testing.assert_array_equal(g[k][:r1], g1[k], err_msg=k)
