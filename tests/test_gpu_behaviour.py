@@ -95,6 +95,36 @@ def test_graph_replay_of_mixed_row_counts(max_rows):
     assert h.get_error() == binding.OK
 
 
+def test_graph_replay_above_16_rows():
+    """Calls of more than 16 rows (two launches each) captured in one graph
+    with a 5-row call between them: every replay equals the eager results."""
+    t = pytest.importorskip("torch")
+    cfg = synth.CONFIGS["c1"].with_rows(24)
+    w = weights("c1")
+    x, r, _ = gapped_rows(cfg, w)
+    h = handle_for(cfg, max_rows=32)
+    dw = device_weights("c1")
+    widths = [24, 5, 17]
+    xd, rd = dev(x), dev(r)
+    outs = [t.empty((n, cfg.hidden), dtype=t.int16, device="cuda") for n in widths]
+    eager = [run(h, cfg, dw, x[:n], r[:n], rows=n, debug=False)["out"] for n in widths]
+    s = t.cuda.Stream()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            for n, o in zip(widths, outs):
+                h.run(n, xd, rd, dw["gamma"], dw["router_w"], None, dw["w13_q"], dw["w13_s"], dw["w2_q"], dw["w2_s"],
+                      dw["ws13"], dw["ws2"], o, stream=s.cuda_stream)
+    for rep in range(10):
+        for o in outs:
+            o.fill_(0)
+        g.replay()
+        t.cuda.synchronize()
+        for n, o, e in zip(widths, outs, eager):
+            np.testing.assert_array_equal(o.cpu().numpy().view(np.uint16), e)
+    assert h.get_error() == binding.OK
+
+
 def test_deadline_fault_drill_then_recovery():
     """One workgroup never passes its first wait: the deadline fires, the whole
     launch exits, the error reads ETIMEOUT, and the next call is correct."""
