@@ -39,6 +39,7 @@ import numpy as np
 _S_GAMMA, _S_ROUTER, _S_BIAS, _S_W13Q, _S_W13S, _S_W2Q, _S_W2S = 1, 2, 3, 4, 5, 6, 7
 _S_WS13, _S_WS2, _S_ROWS, _S_TAIL, _S_BASE = 8, 9, 10, 11, 12
 _S_SGATE = 13
+_S_WO, _S_ATTN = 14, 15
 
 SOFTMAX = 0
 SIGMOID_BIAS = 1
@@ -135,6 +136,17 @@ def make_weights(cfg: Config, experts: Optional[int] = None) -> dict:
         w["ws13"] = None
         w["ws2"] = None
     return w
+
+
+def make_out_proj(cfg: Config, attn_dim: Optional[int] = None) -> dict:
+    """One rank's share of the attention output projection: w_o [H, A] ~
+    bf16(N(0, 1/A)) and attention rows attn [rows, A] ~ bf16(N(0, 1)), with A
+    = H / 8 unless given (a square projection split over 8 ranks), each from
+    a stream of its own."""
+    A = cfg.hidden // 8 if attn_dim is None else attn_dim
+    w_o = to_bf16_bits(_rng(cfg, _S_WO).standard_normal((cfg.hidden, A), dtype=np.float32) / np.float32(math.sqrt(A)))
+    attn = to_bf16_bits(_rng(cfg, _S_ATTN).standard_normal((cfg.rows, A), dtype=np.float32))
+    return {"w_o": w_o, "attn": attn}
 
 
 def make_shared_gate(cfg: Config) -> np.ndarray:

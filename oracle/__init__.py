@@ -64,6 +64,8 @@ def lib():
         L.oracle_e4m3.argtypes = [i]
         L.oracle_topk_grouped.restype = None
         L.oracle_topk_grouped.argtypes = [i, i, p, i, i, p]
+        L.oracle_out_proj.restype = None
+        L.oracle_out_proj.argtypes = [i, i, i, p, p, p, p]
         L.oracle_router_keys.restype = i
         L.oracle_router_keys.argtypes = [i, i, i, i, d, i] + [p] * 7
         _lib = L
@@ -187,3 +189,17 @@ def moe_tail(x, r, w: dict, cfg) -> dict:
     if rc != 0:
         raise ValueError("oracle_moe_tail rejected its arguments")
     return o
+
+
+def out_proj(attn: np.ndarray, w_o: np.ndarray):
+    """x = bf16(attn . w_o^T) (bf16 bits [rows, H]) and the unrounded y
+    (float64), for attn [rows, A] and w_o [H, A] in bf16 bits."""
+    attn = np.ascontiguousarray(attn, dtype=np.uint16)
+    w_o = np.ascontiguousarray(w_o, dtype=np.uint16)
+    R, A = attn.shape
+    H = w_o.shape[0]
+    assert w_o.shape[1] == A
+    y = np.zeros((R, H), dtype=np.float64)
+    x = np.zeros((R, H), dtype=np.uint16)
+    lib().oracle_out_proj(R, A, H, _ptr(attn), _ptr(w_o), _ptr(y), _ptr(x))
+    return x, y

@@ -29,6 +29,8 @@
  *            sums: l[e] = rstd * sum_i hg[i] Wr[e, i], likewise g and u of the
  *            shared expert; the routed experts and the gate still take xn
  *   y      = sum_k w_k d_{S_k} + s ;   out = bf16(h + y)
+ *   front (optional, oracle_out_proj): x = bf16(attn . W_o^T), one rank's
+ *            share of the attention output projection
  *
  * Sources (page titles; no listing is followed line by line):
  *   - "[AMD] integrate kimi k3 monokernel" (sglang PR 43481), K2 commit text,
@@ -375,6 +377,26 @@ int oracle_moe_tail(int rows, int H, int E, int K, int I, int Is, int scoring, d
   }
   free(h); free(xn); free(hg); free(lg); free(ky); free(ids); free(w); free(d); free(yr); free(ys);
   return 0;
+}
+
+/* The out_proj in front of the tail, on one tensor-parallel rank's share
+ * ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation and
+ * Modifications: the fused launch starts with the attention output
+ * projection, whose result is all-reduced over the ranks before the norm).
+ * attn [rows, A] bf16 is this rank's slice of the attention output and w_o
+ * [H, A] bf16 the matching columns of the projection: y = attn . w_o^T in
+ * double, and x = bf16(y) is the tail's input row.  On one GPU the rank's
+ * partial stands for the all-reduced sum (the reduce itself is not run).
+ * y_out may be NULL. */
+void oracle_out_proj(int rows, int A, int H, const uint16_t* attn, const uint16_t* w_o, double* y_out,
+                     uint16_t* x_out) {
+  for (int r = 0; r < rows; r++)
+    for (int h = 0; h < H; h++) {
+      double acc = 0.0;
+      for (int a = 0; a < A; a++) acc += bfd(attn, (size_t)r * A + a) * bfd(w_o, (size_t)h * A + a);
+      if (y_out) y_out[(size_t)r * H + h] = acc;
+      x_out[(size_t)r * H + h] = oracle_bf16_round(acc);
+    }
 }
 
 /* Norm + router + keys only (used to check the top-k gap of generated rows). */

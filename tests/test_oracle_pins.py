@@ -634,3 +634,63 @@ def test_folded_norm_leaves_the_routed_experts_on_xn():
     np.testing.assert_array_equal(of["xn"], o["xn"])
     np.testing.assert_array_equal(of["h"], o["h"])
     assert not np.array_equal(of["y_shared"], o["y_shared"])
+
+
+# ---- the out_proj front ----------------------------------------------------------
+
+def test_out_proj_one_hot_row_reads_a_column_exactly():
+    """An attention row that is 1 at column a and 0 elsewhere projects to
+    column a of w_o, bit for bit (one exact product per output, no rounding)."""
+    cfg = synth.CONFIGS["c0"].with_rows(3)
+    w_o = synth.make_out_proj(cfg)["w_o"]
+    A = w_o.shape[1]
+    attn = np.zeros((3, A), np.uint16)
+    cols = [0, A // 2 + 1, A - 1]
+    for r, a in enumerate(cols):
+        attn[r, a] = 0x3F80  # 1.0
+    x, _ = oracle.out_proj(attn, w_o)
+    for r, a in enumerate(cols):
+        np.testing.assert_array_equal(x[r], w_o[:, a])
+
+
+def test_out_proj_is_the_matrix_product_then_one_rounding():
+    """y equals the float64 matrix product (a library routine, another
+    summation order), and x is y rounded to bf16 once: it matches the float32
+    route wherever float32 holds y exactly enough to round the same way, and
+    never misses by more than one bf16 step."""
+    cfg = synth.CONFIGS["c3"].with_rows(4)
+    f = synth.make_out_proj(cfg)
+    x, y = oracle.out_proj(f["attn"], f["w_o"])
+    a64 = synth.bf16_bits_to_f32(f["attn"]).astype(np.float64)
+    w64 = synth.bf16_bits_to_f32(f["w_o"]).astype(np.float64)
+    ref = a64 @ w64.T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    for v, b in zip(y.ravel()[:2000], x.ravel()[:2000]):
+        assert int(b) == oracle.bf16_round(float(v))
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    step = np.abs(xf) * 2.0**-7 + 1e-30
+    assert np.all(np.abs(xf - ref) <= step)
+
+
+def test_out_proj_scales_by_powers_of_two_exactly():
+    """Doubling the attention rows doubles every output exactly: the products,
+    the sum and the bf16 rounding all commute with a factor of 2."""
+    cfg = synth.CONFIGS["c0"].with_rows(2)
+    f = synth.make_out_proj(cfg)
+    attn2 = (f["attn"] + np.uint16(1 << 7) * ((f["attn"] & 0x7F80) != 0)).astype(np.uint16)
+    x1, y1 = oracle.out_proj(f["attn"], f["w_o"])
+    x2, y2 = oracle.out_proj(attn2, f["w_o"])
+    np.testing.assert_array_equal(y2, 2 * y1)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(x2), 2 * synth.bf16_bits_to_f32(x1))
+
+
+def test_out_proj_rounds_once_from_the_exact_sum():
+    """y = 1 + 2^-8 + 2^-30 (three exact products) lies just above a bf16
+    halfway point: rounded once it is 1 + 2^-7 (0x3F81).  A route through
+    float32 would land on the halfway point and round to even (0x3F80)."""
+    b = lambda v: int(synth.to_bf16_bits(np.array([v], np.float32))[0])
+    attn = np.array([[b(1.0), b(1.0), b(1.0)]], np.uint16)
+    w_o = np.array([[b(1.0), b(2.0**-8), b(2.0**-30)]], np.uint16)
+    x, y = oracle.out_proj(attn, w_o)
+    assert y[0, 0] == 1 + 2.0**-8 + 2.0**-30
+    assert int(x[0, 0]) == 0x3F81
