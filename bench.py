@@ -81,22 +81,28 @@ def per_expert_bytes(cfg):
     return 2 * I * H // cb + 2 * I * H // 32 + H * I // cb + H * I // 32
 
 
-def alg_bytes(cfg, rows, distinct):
+def alg_bytes(cfg, rows, distinct, attn_dim=0):
     H, E, Is = cfg.hidden, cfg.experts, cfg.shared_inter
     b = distinct * per_expert_bytes(cfg) + E * H * 2 + 3 * Is * H * 2 + H * 2
     if cfg.scoring == synth.SIGMOID_BIAS:
         b += E * 4
     b += rows * H * 2 * 4  # x, residual in; out, res_out out
+    if attn_dim:  # the out_proj front: w_o and the attention rows in place of x
+        b += H * attn_dim * 2 + rows * attn_dim * 2 - rows * H * 2
     return b
 
 
 class Workload:
     """Device copies of one config's weights and rows, and a handle."""
 
-    def __init__(self, cfg, rows, copies, torch):
+    def __init__(self, cfg, rows, copies, torch, front=False):
         self.t = torch
         self.cfg = cfg.with_rows(rows)
         w = synth.make_weights(cfg)
+        self.attn_dim = 0
+        if front:  # one rank's share of a square out_proj (A = H / 8)
+            f = synth.make_out_proj(self.cfg)
+            w["w_o"], self.attn_dim = f["w_o"], f["w_o"].shape[1]
         rho = c2_rho() if cfg.similar else 0.0
         x, r = synth.make_rows(self.cfg, rho=rho)
         dev = lambda a: None if a is None else torch.from_numpy(
@@ -105,20 +111,21 @@ class Workload:
         del w
         self.copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(copies - 1)]
         self.x, self.r = dev(x), dev(r)
+        self.attn = dev(f["attn"]) if front else None
         H = cfg.hidden
         self.out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
         self.res_out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
         self.ids = torch.empty((rows, cfg.topk), dtype=torch.int32, device="cuda")
         c = binding.make_config(rows, H, cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter, cfg.scoring, cfg.eps,
-                                weight_format=cfg.weight_format, fold_norm=cfg.fold_norm)
+                                weight_format=cfg.weight_format, fold_norm=cfg.fold_norm, attn_dim=self.attn_dim)
         self.h = binding.MoeTail(c)
         self.rows = rows
 
     def call(self, i, stream, ids=False):
         d = self.copies[i % len(self.copies)]
-        self.h.run(self.rows, self.x, self.r, d["gamma"], d["router_w"], d["router_bias"], d["w13_q"], d["w13_s"],
-                   d["w2_q"], d["w2_s"], d["ws13"], d["ws2"], self.out, self.res_out,
-                   self.ids if ids else None, None, stream=stream.cuda_stream)
+        self.h.run(self.rows, None if self.attn_dim else self.x, self.r, d["gamma"], d["router_w"], d["router_bias"],
+                   d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], d["ws13"], d["ws2"], self.out, self.res_out,
+                   self.ids if ids else None, None, stream=stream.cuda_stream, attn=self.attn, w_o=d.get("w_o"))
 
     def distinct(self, stream):
         self.call(0, stream, ids=True)
@@ -242,6 +249,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
     ap.add_argument("--fp8", action="store_true", help="with --only: MXFP8 (E4M3) routed experts")
     ap.add_argument("--fold", action="store_true", help="with --only: the norm folded into the router/shared sums")
+    ap.add_argument("--front", action="store_true", help="with --only: the out_proj front (attention rows in, A = H/8)")
     ap.add_argument("--calib", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -262,16 +270,17 @@ def main():
         print(json.dumps({"calib_copy_bytes": a.numel(), "copies": 10}))
         return
 
-    def measure(name, rows, fmt=0, fold=0):
+    def measure(name, rows, fmt=0, fold=0, front=False):
         cfg = dataclasses.replace(cfgs[name], weight_format=fmt, fold_norm=fold)
         guess = {1: 10, 2: 20, 4: 39, 8: 56, 16: 139}.get(rows, rows * cfg.topk)
         L = copies_for(cfg, rows, guess)
-        wl = Workload(cfg, rows, L, torch)
+        wl = Workload(cfg, rows, L, torch, front=front)
         s = torch.cuda.Stream()
         dist = wl.distinct(s)
         us = wl.time_eager(args.steps, args.warmup) if args.eager else wl.time(args.steps, args.warmup)
-        B = alg_bytes(cfg, rows, dist)
-        rec = {"workload": name + ("-mxfp8" if fmt else "") + ("-fold" if fold else ""), "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
+        B = alg_bytes(cfg, rows, dist, wl.attn_dim)
+        rec = {"workload": name + ("-mxfp8" if fmt else "") + ("-fold" if fold else "") + ("-front" if front else ""),
+               "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
                "us_per_call": round(us, 3), "GBps": round(B / (us * 1e-6) / 1e9, 1),
                "frac_of_peak": round(B / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
         print(json.dumps(rec), file=sys.stderr, flush=True)
@@ -281,7 +290,7 @@ def main():
 
     if args.only:
         name, _, rows = args.only.partition(":")
-        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0)
+        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0, args.front)
         return
 
     head = measure("c2", 8)
@@ -296,6 +305,7 @@ def main():
         sweep.append(measure("c2", 8, 0, 1))
         sweep.append(measure("c1", 1, 0, 1))
         sweep.append(measure("c1", 32))
+        sweep.append(measure("c2", 8, front=True))
     copy_gbps = copy_bandwidth(torch)
     cpu = cpu_baseline(cfgs["c2"]) if args.cpu else None
     us = head["us_per_call"]

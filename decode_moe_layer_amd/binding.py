@@ -30,14 +30,15 @@ class Config(ctypes.Structure):
         ("scoring", ctypes.c_int32), ("eps", ctypes.c_float), ("device", ctypes.c_int32),
         ("deadline_us", ctypes.c_uint32), ("debug_flags", ctypes.c_uint32), ("debug_block", ctypes.c_int32),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("routed_scale", ctypes.c_float),
-        ("weight_format", ctypes.c_int32), ("fold_norm", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32), ("fold_norm", ctypes.c_int32), ("attn_dim", ctypes.c_int32),
     ]
 
 
 class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "residual", "gamma", "router_w", "router_bias", "w13_q", "w13_s", "w2_q", "w2_s", "ws13", "ws2",
-        "out", "res_out", "topk_ids", "topk_w", "dbg_logits", "dbg_y_routed", "dbg_y_shared", "shared_gate")]
+        "out", "res_out", "topk_ids", "topk_w", "dbg_logits", "dbg_y_routed", "dbg_y_shared", "shared_gate", "attn",
+        "w_o")]
 
 
 class MoeTailError(RuntimeError):
@@ -74,9 +75,9 @@ def lib():
 
 def make_config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring=SOFTMAX, eps=1e-6,
                 device=-1, deadline_us=0, debug_flags=0, debug_block=0, n_group=1, topk_group=1,
-                routed_scale=1.0, weight_format=MXFP4, fold_norm=0) -> Config:
+                routed_scale=1.0, weight_format=MXFP4, fold_norm=0, attn_dim=0) -> Config:
     return Config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring, eps, device, deadline_us,
-                  debug_flags, debug_block, n_group, topk_group, routed_scale, weight_format, fold_norm)
+                  debug_flags, debug_block, n_group, topk_group, routed_scale, weight_format, fold_norm, attn_dim)
 
 
 def check_config(cfg: Config) -> int:
@@ -109,11 +110,12 @@ class MoeTail:
 
     def run(self, rows, x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13, ws2, out,
             res_out=None, topk_ids=None, topk_w=None, dbg_logits=None, dbg_y_routed=None, dbg_y_shared=None,
-            stream=None, shared_gate=None):
-        """Enqueue one call; tensors are torch device tensors (or raw device addresses)."""
+            stream=None, shared_gate=None, attn=None, w_o=None):
+        """Enqueue one call; tensors are torch device tensors (or raw device addresses).
+        With attn (and w_o) the library computes x itself (the out_proj front); pass x=None."""
         a = Args(*[_ptr(t) for t in (x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13,
                                      ws2, out, res_out, topk_ids, topk_w, dbg_logits, dbg_y_routed, dbg_y_shared,
-                                     shared_gate)])
+                                     shared_gate, attn, w_o)])
         if stream is None:
             import torch
 

@@ -1550,6 +1550,66 @@ static const void* kernel_for(const Params& p) {
   return f ? (const void*)moe_tail_kernel_lds_f : (const void*)moe_tail_kernel_lds;
 }
 
+// The out_proj front: x[r][h] = bf16(sum_a attn[r][a] w_o[h][a]).  Every
+// bf16 product is exact in double and the sum is taken in double, then
+// rounded to bf16 once, as the projection's definition asks; the work is a
+// few MB of weights, so plain vector loads and fp64 FMAs are enough.  A
+// workgroup of 256 threads owns OP_H output columns h for up to MAX_R rows
+// (blockIdx.y selects the row block): thread (hi, ks) sums K elements
+// ks*8 + OP_KS*8*j .. +7 (OP_KS lanes read contiguous bytes of a weight row
+// per step, and each thread has only A / (8 OP_KS) steps of load latency),
+// and the OP_KS slices are added in order.
+constexpr int OP_NT = 256, OP_KS = 64, OP_H = OP_NT / OP_KS;
+__global__ __launch_bounds__(OP_NT) void moe_tail_out_proj_kernel(const uint16_t* attn, const uint16_t* w_o,
+                                                                   uint16_t* x, int rows, int A, int H) {
+  __shared__ double part[OP_KS][OP_H][MAX_R + 1];  // [slice][column][row]
+  const int tid = threadIdx.x, ks = tid % OP_KS, hi = tid / OP_KS;
+  const int h = blockIdx.x * OP_H + hi;
+  const int r0 = blockIdx.y * MAX_R, R = min(MAX_R, rows - r0);
+  attn += (size_t)r0 * A;
+  x += (size_t)r0 * H;
+  const rsrc_t rw = make_rsrc(w_o, (uint32_t)((size_t)H * A * 2));
+  const rsrc_t ra = make_rsrc(attn, (uint32_t)((size_t)R * A * 2));
+  double acc[MAX_R];
+#pragma unroll
+  for (int r = 0; r < MAX_R; ++r) acc[r] = 0.0;
+#pragma unroll 2
+  for (int a0 = ks * 8; a0 < A; a0 += OP_KS * 8) {
+    const u32x4 wv = ld16<0>(rw, h < H ? (uint32_t)(h * A + a0) * 2u : OOB);
+    u32x4 av[MAX_R];
+#pragma unroll
+    for (int r = 0; r < MAX_R; ++r)
+      if (r < R) av[r] = ld16<0>(ra, (uint32_t)(r * A + a0) * 2u);
+    double wd[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      wd[2 * c] = (double)bf2f(wv[c] & 0xFFFFu);
+      wd[2 * c + 1] = (double)bf2f(wv[c] >> 16);
+    }
+#pragma unroll
+    for (int r = 0; r < MAX_R; ++r) {
+      if (r < R) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[r] = fma(wd[2 * c], (double)bf2f(av[r][c] & 0xFFFFu), acc[r]);
+          acc[r] = fma(wd[2 * c + 1], (double)bf2f(av[r][c] >> 16), acc[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < MAX_R; ++r) part[ks][hi][r] = acc[r];
+  __syncthreads();
+  if (tid < OP_H * MAX_R) {
+    const int r = tid % MAX_R, hc = tid / MAX_R, ho = blockIdx.x * OP_H + hc;
+    if (r < R && ho < H) {
+      double sum = 0.0;
+      for (int k = 0; k < OP_KS; ++k) sum += part[k][hc][r];
+      x[(size_t)r * H + ho] = (uint16_t)d2bf(sum);
+    }
+  }
+}
+
 }  // namespace mt
 
 // ==================================================================== host ==
@@ -1615,6 +1675,7 @@ struct moe_tail {
   int S1, TC, n_rb, n_sb, Ep;
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
   int max_rows_call;  // the caller's max_rows (cfg.max_rows is the per-launch one, at most MAX_R)
+  uint16_t* xbuf;     // [max_rows_call, H] bf16: x computed by the out_proj front (attn_dim > 0)
   char err[256];
 };
 
@@ -1653,6 +1714,8 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
                          c->top_k > c->topk_group * (c->num_experts / c->n_group)))
     return fail(nullptr, MOE_TAIL_EINVAL, "topk_group %d must be in 1..n_group and keep at least top_k experts",
                 c->topk_group);
+  if (c->attn_dim < 0 || c->attn_dim > 16384 || c->attn_dim % 128)
+    return fail(nullptr, MOE_TAIL_EINVAL, "attn_dim %d must be 0 or a multiple of 128 up to 16384", c->attn_dim);
   if (c->fold_norm != 0 && c->fold_norm != 1)
     return fail(nullptr, MOE_TAIL_EINVAL, "fold_norm %d must be 0 or 1", c->fold_norm);
   if (c->weight_format != MOE_TAIL_MXFP4 && c->weight_format != MOE_TAIL_MXFP8)
@@ -1728,7 +1791,8 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_xnt = o_xn + al(R * H * 2);
   const size_t o_lg = o_xnt + al(R * H * 4), o_pt = o_lg + al(R * (size_t)h->Ep * 8);
   const size_t o_gp = o_pt + al((size_t)n_it * 2048), o_rs = o_gp + al(R * mt::NQ * 8), o_as = o_rs + al(R * 8);
-  const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), total = o_ar + al(R * K * I * 2);
+  const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), o_xb = o_ar + al(R * K * I * 2);
+  const size_t total = o_xb + (cfg->attn_dim > 0 ? al((size_t)max_rows_call * H * 2) : 0);
   (void)E;
   int prev = 0;
   (void)hipGetDevice(&prev);
@@ -1768,6 +1832,7 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
   h->scratch_bytes = total;
   h->a_s = (uint16_t*)(base + o_as);
   h->a_r = (uint16_t*)(base + o_ar);
+  h->xbuf = cfg->attn_dim > 0 ? (uint16_t*)(base + o_xb) : nullptr;
   snprintf(h->err, sizeof(h->err), "no error");
   *out = h;
   return MOE_TAIL_OK;
@@ -1889,6 +1954,21 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   if (!a) return fail(h, MOE_TAIL_EINVAL, "args is NULL");
   if (rows < 1 || rows > h->max_rows_call)
     return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, h->max_rows_call);
+  moe_tail_args fa;
+  if (a->attn) {  // the out_proj front: x = bf16(attn . w_o^T) into handle scratch, then the tail on it
+    if (a->x) return fail(h, MOE_TAIL_EINVAL, "give x or attn, not both");
+    if (!h->xbuf) return fail(h, MOE_TAIL_EINVAL, "attn needs a handle created with attn_dim > 0");
+    if (!a->w_o) return fail(h, MOE_TAIL_EINVAL, "w_o is required with attn");
+    if (!aligned(a->attn, 16) || !aligned(a->w_o, 16)) return fail(h, MOE_TAIL_EINVAL, "attn/w_o are not 16-byte aligned");
+    const int H = h->cfg.hidden;
+    hipLaunchKernelGGL(mt::moe_tail_out_proj_kernel, dim3((H + mt::OP_H - 1) / mt::OP_H, (rows + mt::MAX_R - 1) / mt::MAX_R),
+                       dim3(mt::OP_NT), 0, (hipStream_t)stream,
+                       (const uint16_t*)a->attn, (const uint16_t*)a->w_o, h->xbuf, rows, h->cfg.attn_dim, H);
+    HIPCHK(h, hipGetLastError());
+    fa = *a;
+    fa.x = h->xbuf;
+    a = &fa;
+  }
   if (rows <= mt::MAX_R) return run_launch(h, rows, a, stream);
   // More rows than one launch's MFMA columns: balanced row ranges, one
   // launch each, in order on the stream (each streams its own experts)

@@ -94,6 +94,8 @@ typedef struct {
                             Long-context indexer ...", PR 85 commit text: the router's norm moves into its
                             logits; not bitwise equal to projecting xn).  The routed experts and the shared
                             gate still take xn.  0: plain (the router and shared expert project xn) */
+  int32_t attn_dim;      /* A of the out_proj front: 0 (none), or a multiple of 128 up to 16384.  With A > 0
+                            a call may pass attention rows instead of x (see moe_tail_args.attn) */
 } moe_tail_config;
 
 typedef struct {
@@ -123,6 +125,13 @@ typedef struct {
                                scaled by sigmoid(wg . xn) per row ("[AMD] integrate kimi k3
                                monokernel", K2 commit text, Kernel Replacement: the fused
                                gate-sigmoid-mul-add on the shared expert); ignored when Is == 0 */
+  /* the out_proj front ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation and
+     Modifications: the fused launch starts with the attention output projection).  When attn is
+     given, x must be NULL: the library first computes x = bf16(attn . w_o^T) per row, the sum in
+     double and rounded once, into handle scratch (a launch of its own before the tail), and the
+     tail takes that x.  One rank's share: on one GPU its partial stands for the all-reduced sum. */
+  const void* attn;         /* [rows, A] bf16 attention output rows (this rank's slice), or NULL */
+  const void* w_o;          /* [H, A] bf16 out_proj columns of this rank, required with attn */
 } moe_tail_args;
 
 /* Validate a configuration on the host only (no GPU call).  Returns

@@ -37,12 +37,13 @@ def handle_for(cfg, max_rows=None, **kw):
     return binding.MoeTail(c)
 
 
-def run(handle, cfg, dw, x, r, rows=None, stream=None, debug=True):
-    """One call; returns a dict of numpy outputs."""
+def run(handle, cfg, dw, x, r, rows=None, stream=None, debug=True, front=None):
+    """One call; returns a dict of numpy outputs.  front = (attn, w_o) device
+    tensors runs the out_proj front instead of passing x (x may then be None)."""
     t = torch()
-    R = x.shape[0] if rows is None else rows
+    R = (x.shape[0] if front is None else front[0].shape[0]) if rows is None else rows
     H, E, K = cfg.hidden, cfg.experts, cfg.topk
-    xd, rd = dev(x), dev(r) if r is not None else None
+    xd, rd = (dev(x) if x is not None else None), dev(r) if r is not None else None
     o = {
         "out": t.empty((R, H), dtype=t.int16, device="cuda"),
         "res_out": t.empty((R, H), dtype=t.int16, device="cuda"),
@@ -56,7 +57,8 @@ def run(handle, cfg, dw, x, r, rows=None, stream=None, debug=True):
     handle.run(R, xd, rd, dw["gamma"], dw["router_w"], dw.get("router_bias"), dw["w13_q"], dw["w13_s"], dw["w2_q"],
                dw["w2_s"], dw.get("ws13"), dw.get("ws2"), o["out"], o["res_out"], o["ids"], o["w"],
                o.get("logits"), o.get("y_routed"), o.get("y_shared"), stream=stream,
-               shared_gate=dw.get("shared_gate"))
+               shared_gate=dw.get("shared_gate"), attn=None if front is None else front[0],
+               w_o=None if front is None else front[1])
     t.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in o.items()}
     res["out"] = res["out"].view(np.uint16)
