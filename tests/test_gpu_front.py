@@ -30,11 +30,12 @@ def _front_rows(cfg, w, A):
 
 
 @pytest.mark.parametrize("name,rows,A", [("c0", 2, 128), ("c1", 8, 768), ("c3", 4, 896), ("c4", 16, 1024),
-                                         ("c1", 20, 768)])
+                                         ("c1", 20, 768), ("c0", 32, 16384)])
 def test_front_parity(name, rows, A):
     """x bit for bit and the whole tail to the usual bars: c0 with A = 128,
     the 512-expert shard at 8 rows, sigmoid keys, 16 rows from global
-    scratch, and a 20-row call (two tail launches on one front)."""
+    scratch, a 20-row call (two tail launches on one front), and the largest
+    accepted width A = 16384 at 32 rows (two row blocks in the front)."""
     cfg = synth.CONFIGS[name].with_rows(rows)
     print("front", name, rows, A, flush=True)
     w = weights(name)
