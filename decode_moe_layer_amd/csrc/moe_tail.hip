@@ -1564,7 +1564,7 @@ static const void* kernel_for(const Params& p) {
 // ks*8 + OP_KS*8*j .. +7 (OP_KS lanes read contiguous bytes of a weight row
 // per step, and each thread has only A / (8 OP_KS) steps of load latency),
 // and the OP_KS slices are added in order.
-constexpr int OP_NT = 256, OP_KS = 64, OP_H = OP_NT / OP_KS;
+constexpr int OP_NT = 256, OP_KS = 32, OP_H = OP_NT / OP_KS;
 __global__ __launch_bounds__(OP_NT) void moe_tail_out_proj_kernel(const uint16_t* attn, const uint16_t* w_o,
                                                                    uint16_t* x, int rows, int A, int H) {
   __shared__ double part[OP_KS][OP_H][MAX_R + 1];  // [slice][column][row]
