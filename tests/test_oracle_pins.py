@@ -694,3 +694,47 @@ def test_out_proj_rounds_once_from_the_exact_sum():
     x, y = oracle.out_proj(attn, w_o)
     assert y[0, 0] == 1 + 2.0**-8 + 2.0**-30
     assert int(x[0, 0]) == 0x3F81
+
+
+def e4m3_from_bits(code: int) -> float:
+    """E4M3 from its bit fields (OCP MX v1.0): sign bit 7, exponent bits 6..3
+    with bias 7, mantissa bits 2..0; exponent 0 is subnormal (2^-6 m/8)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    return s * (2.0 ** -6 * m / 8 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8))
+
+
+def test_one_expert_one_row_closed_form_mxfp8():
+    """The same closed form as for MXFP4, with MXFP8 codes drawn from all 254
+    non-NaN E4M3 codes (subnormals, both signs, up to 448): xn = 1 exactly, so
+    g_i = H v_g[i] 2^(s_g-127), u_i = H v_u[i] 2^(s_u-127) and
+    out_h = bf16(1 + v_d[h] 2^(s_d-127) sum_i silu(g_i) u_i)."""
+    import dataclasses
+
+    H, I = 256, 64
+    cfg = dataclasses.replace(_cfg(H, 1, 1, I, 0), weight_format=1)
+    w = _zero_weights(cfg)
+    w["w13_q"] = np.zeros((1, 2 * I, H), np.uint8)
+    w["w2_q"] = np.zeros((1, H, I), np.uint8)
+    rng = np.random.default_rng(9)
+    ok = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    cg, cu, cd = rng.choice(ok, I), rng.choice(ok, I), rng.choice(ok, H)
+    sg, su, sd = 110, 112, 115
+    w["w13_q"][0, :I, :] = cg[:, None]
+    w["w13_q"][0, I:, :] = cu[:, None]
+    w["w13_s"][0, :I, :] = sg
+    w["w13_s"][0, I:, :] = su
+    w["w2_q"][0, :, :] = cd[:, None]
+    w["w2_s"][0] = sd
+    x = bf16(np.ones((1, H)))
+    o = oracle.moe_tail(x, None, w, cfg)
+    assert np.all(o["xn"] == 0x3F80)
+    acc = 0.0
+    for i in range(I):
+        g = H * e4m3_from_bits(int(cg[i])) * 2.0 ** (sg - 127)
+        u = H * e4m3_from_bits(int(cu[i])) * 2.0 ** (su - 127)
+        acc += silu(g) * u
+    d = np.array([e4m3_from_bits(int(cd[h])) * 2.0 ** (sd - 127) * acc for h in range(H)])
+    np.testing.assert_allclose(o["y_routed"][0], d, rtol=1e-12, atol=1e-300)
+    want = np.array([oracle.bf16_round(1.0 + v) for v in d], np.uint16)
+    np.testing.assert_array_equal(o["out"][0], want)
