@@ -95,10 +95,12 @@ def alg_bytes(cfg, rows, distinct, attn_dim=0):
 class Workload:
     """Device copies of one config's weights and rows, and a handle."""
 
-    def __init__(self, cfg, rows, copies, torch, front=False):
+    def __init__(self, cfg, rows, copies, torch, front=False, shuf=False):
         self.t = torch
         self.cfg = cfg.with_rows(rows)
         w = synth.make_weights(cfg)
+        if shuf:  # the same codes in the unit-blocked gate/up layout
+            w["w13_q"] = synth.w13_unit_blocked(w["w13_q"], cfg.inter)
         self.attn_dim = 0
         if front:  # one rank's share of a square out_proj (A = H / 8)
             f = synth.make_out_proj(self.cfg)
@@ -117,7 +119,8 @@ class Workload:
         self.res_out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
         self.ids = torch.empty((rows, cfg.topk), dtype=torch.int32, device="cuda")
         c = binding.make_config(rows, H, cfg.experts, cfg.topk, cfg.inter, cfg.shared_inter, cfg.scoring, cfg.eps,
-                                weight_format=cfg.weight_format, fold_norm=cfg.fold_norm, attn_dim=self.attn_dim)
+                                weight_format=cfg.weight_format, fold_norm=cfg.fold_norm, attn_dim=self.attn_dim,
+                                w13_layout=1 if shuf else 0)
         self.h = binding.MoeTail(c)
         self.rows = rows
 
@@ -249,6 +252,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="direct launches instead of graph replay (profiling)")
     ap.add_argument("--fp8", action="store_true", help="with --only: MXFP8 (E4M3) routed experts")
     ap.add_argument("--fold", action="store_true", help="with --only: the norm folded into the router/shared sums")
+    ap.add_argument("--shuf", action="store_true", help="with --only: MXFP4 gate/up codes in the unit-blocked layout")
     ap.add_argument("--front", action="store_true", help="with --only: the out_proj front (attention rows in, A = H/8)")
     ap.add_argument("--calib", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (scale for the HBM byte counters)")
@@ -270,16 +274,16 @@ def main():
         print(json.dumps({"calib_copy_bytes": a.numel(), "copies": 10}))
         return
 
-    def measure(name, rows, fmt=0, fold=0, front=False):
+    def measure(name, rows, fmt=0, fold=0, front=False, shuf=False):
         cfg = dataclasses.replace(cfgs[name], weight_format=fmt, fold_norm=fold)
         guess = {1: 10, 2: 20, 4: 39, 8: 56, 16: 139}.get(rows, rows * cfg.topk)
         L = copies_for(cfg, rows, guess)
-        wl = Workload(cfg, rows, L, torch, front=front)
+        wl = Workload(cfg, rows, L, torch, front=front, shuf=shuf)
         s = torch.cuda.Stream()
         dist = wl.distinct(s)
         us = wl.time_eager(args.steps, args.warmup) if args.eager else wl.time(args.steps, args.warmup)
         B = alg_bytes(cfg, rows, dist, wl.attn_dim)
-        rec = {"workload": name + ("-mxfp8" if fmt else "") + ("-fold" if fold else "") + ("-front" if front else ""),
+        rec = {"workload": name + ("-mxfp8" if fmt else "") + ("-fold" if fold else "") + ("-front" if front else "") + ("-blocked" if shuf else ""),
                "rows": rows, "copies": L, "distinct_experts": dist, "alg_bytes": B,
                "us_per_call": round(us, 3), "GBps": round(B / (us * 1e-6) / 1e9, 1),
                "frac_of_peak": round(B / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
@@ -290,7 +294,7 @@ def main():
 
     if args.only:
         name, _, rows = args.only.partition(":")
-        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0, args.front)
+        measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0, args.front, args.shuf)
         return
 
     head = measure("c2", 8)

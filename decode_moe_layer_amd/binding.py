@@ -31,6 +31,7 @@ class Config(ctypes.Structure):
         ("deadline_us", ctypes.c_uint32), ("debug_flags", ctypes.c_uint32), ("debug_block", ctypes.c_int32),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("routed_scale", ctypes.c_float),
         ("weight_format", ctypes.c_int32), ("fold_norm", ctypes.c_int32), ("attn_dim", ctypes.c_int32),
+        ("w13_layout", ctypes.c_int32),
     ]
 
 
@@ -75,9 +76,10 @@ def lib():
 
 def make_config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring=SOFTMAX, eps=1e-6,
                 device=-1, deadline_us=0, debug_flags=0, debug_block=0, n_group=1, topk_group=1,
-                routed_scale=1.0, weight_format=MXFP4, fold_norm=0, attn_dim=0) -> Config:
+                routed_scale=1.0, weight_format=MXFP4, fold_norm=0, attn_dim=0, w13_layout=0) -> Config:
     return Config(max_rows, hidden, num_experts, top_k, inter, shared_inter, scoring, eps, device, deadline_us,
-                  debug_flags, debug_block, n_group, topk_group, routed_scale, weight_format, fold_norm, attn_dim)
+                  debug_flags, debug_block, n_group, topk_group, routed_scale, weight_format, fold_norm, attn_dim,
+                  w13_layout)
 
 
 def check_config(cfg: Config) -> int:

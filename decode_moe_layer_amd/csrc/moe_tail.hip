@@ -120,6 +120,7 @@ struct Params {
   int n_group, topk_group;  // group-limited routing (n_group 1: none)
   int f8;                   // routed experts in MXFP8 (E4M3 codes), else MXFP4
   int fold;                 // rstd multiplies the router and shared gate/up sums over bf16(h * gamma)
+  int shuf;                 // MXFP4 w13 codes in the unit-blocked layout (one 1 KB block per wave load)
   float rscale;             // routed scaling factor
   int xn_lds;                     // activations staged in LDS (else read from global scratch)
   int rsum;                       // top-k readers sum the router K-chunk partials themselves
@@ -1183,11 +1184,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const rsrc_t rs = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
         const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
         const int tb = t02 + CPF * q2, np = min(CPF, TP2 - CPF * q2);
-        const uint32_t qoff = (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16)), soff = (uint32_t)(wrow * (H / 32) + tb * 4);
+        // unit-blocked MXFP4 layout: unit b's column group c is 1 KB, lane-ordered
+        const bool sh = !F8 && p.shuf;
+        const uint32_t qoff = sh ? (uint32_t)(b * T2 * 1024 + lane * 16) : (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
+        const uint32_t soff = (uint32_t)(wrow * (H / 32) + tb * 4), cst = sh ? 1024u : 64u;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = F8 ? j >> 1 : j;
-          const uint32_t o = F8 ? (uint32_t)(tb + t) * 128u + (uint32_t)(j & 1) * 16u : (uint32_t)(tb + t) * 64u;
+          const uint32_t o = F8 ? (uint32_t)(tb + t) * 128u + (uint32_t)(j & 1) * 16u : (uint32_t)(tb + t) * cst;
           f.a[j] = ld16<CP_W>(rq, (v && t < np && tb + t < T2) ? qoff + o : OOB);
         }
         f.s[0] = ld16<CP_W>(rs, v ? soff : OOB);
@@ -1236,14 +1240,16 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       // activations from global memory: one column group per frag, with its B fragments
       int k2 = 0, t2 = t02;
       rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
-      uint32_t qoff = 0, soff = 0, boff = OOB;
+      uint32_t qoff = 0, soff = 0, boff = OOB, qst = F8 ? 128u : 64u;
       auto p2_unit = [&]() {
         const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
         const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
         rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
         rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
         const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
-        qoff = (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
+        const bool sh = !F8 && p.shuf;  // unit-blocked MXFP4 layout
+        qoff = sh ? (uint32_t)(b * T2 * 1024 + lane * 16) : (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
+        qst = sh ? 1024u : (F8 ? 128u : 64u);
         soff = (uint32_t)(wrow * (H / 32));
         const uint32_t mask = S.slot_mask[d];
         boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
@@ -1254,7 +1260,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         const bool v = k2 < nu2 && t2 < T2;
 #pragma unroll
         for (int j = 0; j < (F8 ? 2 : 1); ++j)
-          f.a[j] = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * (F8 ? 128u : 64u) + (uint32_t)j * 16u : OOB);
+          f.a[j] = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * qst + (uint32_t)j * 16u : OOB);
         f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -1721,6 +1727,8 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
                 c->topk_group);
   if (c->attn_dim < 0 || c->attn_dim > 16384 || c->attn_dim % 128)
     return fail(nullptr, MOE_TAIL_EINVAL, "attn_dim %d must be 0 or a multiple of 128 up to 16384", c->attn_dim);
+  if (c->w13_layout != 0 && !(c->w13_layout == 1 && c->weight_format == MOE_TAIL_MXFP4))
+    return fail(nullptr, MOE_TAIL_EINVAL, "w13_layout %d: 0, or 1 with MXFP4 experts", c->w13_layout);
   if (c->fold_norm != 0 && c->fold_norm != 1)
     return fail(nullptr, MOE_TAIL_EINVAL, "fold_norm %d must be 0 or 1", c->fold_norm);
   if (c->weight_format != MOE_TAIL_MXFP4 && c->weight_format != MOE_TAIL_MXFP8)
@@ -1883,6 +1891,7 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.rscale = c.routed_scale > 0.f ? c.routed_scale : 1.f;
   p.f8 = c.weight_format == MOE_TAIL_MXFP8;
   p.fold = c.fold_norm;
+  p.shuf = c.w13_layout == 1;
   p.G = h->G;
   p.xn_lds = h->plan.xn_lds;
   // reader-side router sums when each thread then loads at most 8 partials

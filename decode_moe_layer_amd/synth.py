@@ -149,6 +149,21 @@ def make_out_proj(cfg: Config, attn_dim: Optional[int] = None) -> dict:
     return {"w_o": w_o, "attn": attn}
 
 
+def w13_unit_blocked(w13_q: np.ndarray, inter: int) -> np.ndarray:
+    """Re-lay MXFP4 w13 codes [E, 2I, H/2] into the unit-blocked layout (same
+    shape and bytes, reordered): for unit b (gate rows 8b..8b+7, up rows
+    I+8b..I+8b+7), column group c (64 bytes of a row) and lane l = 16 q + i,
+    16 bytes at ((b * H/128 + c) * 64 + l) * 16 are bytes 16q..16q+15 of
+    column group c of unit row i.  A pure permutation of storage."""
+    E, R2, HB = w13_q.shape
+    I, T2 = inter, HB // 64
+    assert R2 == 2 * I and HB % 64 == 0 and I % 8 == 0
+    i16 = np.arange(16)
+    rows = np.array([[b * 8 + i if i < 8 else I + b * 8 + i - 8 for i in i16] for b in range(I // 8)])
+    x = w13_q[:, rows].reshape(E, I // 8, 16, T2, 4, 16)  # [E, b, i, c, q, byte]
+    return np.ascontiguousarray(x.transpose(0, 1, 3, 4, 2, 5)).reshape(E, R2, HB)
+
+
 def make_shared_gate(cfg: Config) -> np.ndarray:
     """Shared-expert gate weights [H] (bf16 bits) ~ bf16(N(0, 1/hidden)), from a
     stream of their own (the other weights do not change with or without it)."""

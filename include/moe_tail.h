@@ -96,6 +96,12 @@ typedef struct {
                             gate still take xn.  0: plain (the router and shared expert project xn) */
   int32_t attn_dim;      /* A of the out_proj front: 0 (none), or a multiple of 128 up to 16384.  With A > 0
                             a call may pass attention rows instead of x (see moe_tail_args.attn) */
+  int32_t w13_layout;    /* MXFP4 w13_q layout: 0 row-major [E, 2I, H/2]; 1 unit-blocked, in which the
+                            codes a wave loads at once are contiguous: for expert e, unit b (intermediate
+                            indices 8b..8b+7), column group c (elements 128c..128c+127) and lane
+                            l = 16 q + i (q < 4, i < 16), bytes ((b H/128 + c) 64 + l) 16 .. +15 hold bytes
+                            16q .. 16q+15 of column group c of row 8b + i (i < 8, gate) or I + 8b + i - 8
+                            (up).  Same size as row-major; scales keep their layout */
 } moe_tail_config;
 
 typedef struct {

@@ -26,8 +26,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # moe_tail_config: 16 x 4-byte integer fields + 2 floats; moe_tail_args: 21 pointers
-    assert ctypes.sizeof(binding.Config) == 18 * 4
+    # moe_tail_config: 17 x 4-byte integer fields + 2 floats; moe_tail_args: 21 pointers
+    assert ctypes.sizeof(binding.Config) == 19 * 4
     assert ctypes.sizeof(binding.Args) == 21 * 8
 
 
@@ -50,7 +50,7 @@ def test_check_config_accepts_the_workloads():
     ("n_group", 3), ("n_group", 128), ("n_group", -1),
     ("routed_scale", -1.0), ("routed_scale", float("inf")),
     ("weight_format", 2), ("weight_format", -1), ("fold_norm", 2), ("fold_norm", -1),
-    ("attn_dim", -128), ("attn_dim", 100), ("attn_dim", 16512),
+    ("attn_dim", -128), ("attn_dim", 100), ("attn_dim", 16512), ("w13_layout", 2), ("w13_layout", -1),
 ])
 def test_check_config_refusals(field, value):
     c = good()

@@ -262,3 +262,25 @@ def test_parity_above_16_rows(name, rows, max_rows):
     g1 = run(h, cfg.with_rows(r1), device_weights(name), x[:r1], r[:r1])
     for k in ("ids", "w", "out", "res_out", "y_routed", "y_shared", "logits"):
         np.testing.assert_array_equal(g[k][:r1], g1[k], err_msg=k)
+
+
+@pytest.mark.parametrize("name,rows", [("c0", 2), ("c1", 8), ("c3", 4), ("c4", 16)])
+def test_unit_blocked_w13_matches_row_major(name, rows):
+    """The same MXFP4 gate/up codes in the unit-blocked layout give the same
+    GPU outputs, bit for bit, as in the row-major one (every kernel path:
+    routed sums by every reader, xn in LDS, sigmoid keys, xn from global)."""
+    from gpu_harness import dev
+
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    _say("unit-blocked", name, rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    g0 = run(handle_for(cfg), cfg, device_weights(name), x, r)
+    dws = dict(device_weights(name))
+    dws["w13_q"] = dev(synth.w13_unit_blocked(w["w13_q"], cfg.inter))
+    h = handle_for(cfg, w13_layout=1)
+    g1 = run(h, cfg, dws, x, r)
+    assert h.get_error() == 0
+    for k in ("ids", "w", "logits", "y_routed", "y_shared", "out", "res_out"):
+        np.testing.assert_array_equal(g1[k], g0[k], err_msg=k)
+    del dws, h

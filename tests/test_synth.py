@@ -93,3 +93,22 @@ def test_mxfp8_codes_are_never_nan_and_cover_every_other_code():
     assert counts[0x7F] == 0 and counts[0xFF] == 0
     assert np.count_nonzero(counts) == 254
     assert counts.max() < 2 * counts[counts > 0].min()  # roughly uniform
+
+
+def test_unit_blocked_w13_is_the_documented_permutation():
+    """The unit-blocked layout puts, for every (unit, column group, lane), the
+    lane's 16 bytes of its unit row at ((b * H/128 + c) * 64 + l) * 16."""
+    cfg = synth.CONFIGS["c0"]
+    w = synth.make_weights(cfg)["w13_q"]
+    I, H = cfg.inter, cfg.hidden
+    s = synth.w13_unit_blocked(w, I).reshape(w.shape[0], -1)
+    T2 = H // 128
+    for e in (0, w.shape[0] - 1):
+        for b in range(I // 8):
+            for c in range(T2):
+                for lane in (0, 7, 8, 15, 16, 37, 63):
+                    i, q = lane & 15, lane >> 4
+                    row = b * 8 + i if i < 8 else I + b * 8 + i - 8
+                    off = ((b * T2 + c) * 64 + lane) * 16
+                    assert np.array_equal(s[e, off:off + 16], w[e, row, c * 64 + q * 16:c * 64 + q * 16 + 16])
+    assert sorted(s.ravel().tolist()) == sorted(w.ravel().tolist())
