@@ -297,14 +297,16 @@ def main():
         measure(name, int(rows) if rows else cfgs[name].rows, 1 if args.fp8 else 0, 1 if args.fold else 0, args.front, args.shuf)
         return
 
-    head = measure("c2", 8)
+    head = measure("c2", 8, shuf=True)  # MXFP4 gate/up codes in the unit-blocked layout
     sweep = []
     if args.sweep:
         for rows in (1, 2, 4, 16):
             sweep.append(measure("c1", rows))
         sweep.append(head)
+        sweep.append(measure("c2", 8))  # the same with row-major gate/up codes
         sweep.append(measure("c3", 4))
         sweep.append(measure("c4", 16))
+        sweep.append(measure("c4", 16, shuf=True))
         sweep.append(measure("c2", 8, 1))
         sweep.append(measure("c2", 8, 0, 1))
         sweep.append(measure("c1", 1, 0, 1))
@@ -327,7 +329,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "c2: one-rank decode shard, 8 rows, hidden 6144, 512 MXFP4 experts (E2M1, "
-                               "E8M0 block-32), top-10 softmax, I 256, bf16 shared Is 512, ~30% repeated picks",
+                               "E8M0 block-32; gate/up codes in the unit-blocked layout), top-10 softmax, I 256, "
+                               "bf16 shared Is 512, ~30% repeated picks",
                    "rows": 8, "distinct_experts": head["distinct_experts"], "weight_copies": head["copies"]},
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": head["frac_of_peak"], "traffic": measured_traffic(),
