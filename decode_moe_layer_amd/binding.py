@@ -6,8 +6,10 @@ module raises; there is no other implementation to fall back to.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_tail.so")
@@ -49,6 +51,16 @@ class MoeTailError(RuntimeError):
 
 
 _lib = None
+_live = weakref.WeakSet()  # open handles, closed at interpreter exit before the HIP runtime tears down
+
+
+@atexit.register
+def _close_live_handles():
+    for h in list(_live):
+        try:
+            h.close()
+        except Exception:
+            pass
 
 
 def lib():
@@ -109,6 +121,7 @@ class MoeTail:
         if st != OK:
             raise MoeTailError(st, strerror(None))
         self.h = h
+        _live.add(self)
 
     def run(self, rows, x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13, ws2, out,
             res_out=None, topk_ids=None, topk_w=None, dbg_logits=None, dbg_y_routed=None, dbg_y_shared=None,

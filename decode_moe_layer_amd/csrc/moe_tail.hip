@@ -1020,14 +1020,21 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #undef MT_CX
     if (FEAT && p.n_group > 1) {
       // group-limited routing: lanes hold 8 consecutive experts, so a group is
-      // gl aligned lanes.  Their two largest keys merge by a butterfly (every
-      // lane of the group ends with the group's pair), the groups are ranked
-      // by the pair's sum in topk_group rounds (equal sums: the lowest lane,
-      // i.e. the lower group), and the experts of the other groups drop out.
+      // gl consecutive lanes [gb, gb + gl) (gl = E / n_group / 8, any value).
+      // Each lane merges the own top-2 of the group's other lanes, read in gl - 1
+      // rotations that never leave the group, into its pair; every lane of the
+      // group then holds the group's two largest keys (max/min merges, so the
+      // result does not depend on the order).  The groups are ranked by the
+      // pair's sum in topk_group rounds (equal sums: the lowest lane, i.e. the
+      // lower group), and the experts of the other groups drop out.
       const int gl = E / p.n_group / 8;
-      float a1 = key_float((uint32_t)(qv[0] >> 32)), a2 = key_float((uint32_t)(qv[1] >> 32));
-      for (int off = 1; off < gl; off <<= 1) {
-        const float b1 = __shfl_xor(a1, off), b2 = __shfl_xor(a2, off);
+      const int gb = (lane / gl) * gl, li = lane - gb;
+      const float o1 = key_float((uint32_t)(qv[0] >> 32)), o2 = key_float((uint32_t)(qv[1] >> 32));
+      float a1 = o1, a2 = o2;
+      for (int s = 1; s < gl; ++s) {
+        const int src = gb + (li + s < gl ? li + s : li + s - gl);
+        const float b1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(o1)));
+        const float b2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(o2)));
         const float n2 = a1 >= b1 ? fmaxf(b1, a2) : fmaxf(a1, b2);
         a1 = fmaxf(a1, b1);
         a2 = n2;
@@ -1827,12 +1834,36 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
     for (int k = plan.xn_lds ? 0 : 8; k < (plan.xn_lds ? 8 : 12) && e == hipSuccess; ++k)
       e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   }
+  // Every cross-workgroup wait assumes that all G workgroups are resident at
+  // once (one per compute unit); a plain launch relies on it, so each kernel
+  // this handle may launch must fit one workgroup per compute unit with its
+  // LDS, registers and waves.
+  int occ_min = 1 << 30;
+  {
+    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds,     (const void*)mt::moe_tail_kernel_lds_rs,
+                        (const void*)mt::moe_tail_kernel_lds_f,   (const void*)mt::moe_tail_kernel_lds_rs_f,
+                        (const void*)mt::moe_tail_kernel_lds_8,   (const void*)mt::moe_tail_kernel_lds_rs_8,
+                        (const void*)mt::moe_tail_kernel_lds_f8,  (const void*)mt::moe_tail_kernel_lds_rs_f8,
+                        (const void*)mt::moe_tail_kernel_gm,      (const void*)mt::moe_tail_kernel_gm_f,
+                        (const void*)mt::moe_tail_kernel_gm_8,    (const void*)mt::moe_tail_kernel_gm_f8};
+    for (int k = plan.xn_lds ? 0 : 8; k < (plan.xn_lds ? 8 : 12) && e == hipSuccess; ++k) {
+      int nb = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ks[k], mt::NT, dyn);
+      occ_min = nb < occ_min ? nb : occ_min;
+    }
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) {
     (void)hipFree(h->scratch);
     free(h);
     return fail(nullptr, MOE_TAIL_EHIP, "scratch setup: %s", hipGetErrorString(e));
+  }
+  if (occ_min < 1) {
+    (void)hipFree(h->scratch);
+    free(h);
+    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "a workgroup of %d threads with %zu B of dynamic LDS does not fit on a compute unit",
+                mt::NT, dyn);
   }
   char* base = (char*)h->scratch;
   h->ctl = (mt::Ctl*)(base + o_ctl);
@@ -1948,17 +1979,13 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.a_s = h->a_s;
   p.a_r = h->a_r;
 
-  hipStream_t s = (hipStream_t)stream;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  HIPCHK(h, hipStreamIsCapturing(s, &cs));
+  // A plain launch, eager or captured alike: create() has checked that one
+  // workgroup fits on every compute unit, so all G are resident together on
+  // an otherwise idle device; a wait that is never met (another kernel holding
+  // compute units) ends at its deadline with ETIMEOUT instead of hanging.
   void* kargs[] = {&p};
   const void* kern = mt::kernel_for(p);
-  hipError_t e;
-  if (cs == hipStreamCaptureStatusNone)
-    e = hipLaunchCooperativeKernel(kern, dim3(h->G), dim3(mt::NT), kargs,
-                                   (unsigned)h->lds_dyn, s);
-  else
-    e = hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, s);
+  const hipError_t e = hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, (hipStream_t)stream);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "kernel launch: %s", hipGetErrorString(e));
   return MOE_TAIL_OK;
 }

@@ -141,16 +141,32 @@ typedef struct {
 } moe_tail_args;
 
 /* Validate a configuration on the host only (no GPU call).  Returns
- * MOE_TAIL_OK or MOE_TAIL_EINVAL / MOE_TAIL_EUNSUPPORTED. */
+ * MOE_TAIL_OK or MOE_TAIL_EINVAL, with the reason in moe_tail_strerror(NULL).
+ * The pages' fused tail refuses unsupported configurations at start-up rather
+ * than falling back ("[AMD] integrate kimi k3 monokernel", K2 commit text,
+ * section Refusals).  Limits that depend on the device (the compute-unit
+ * count bounds H, LDS bounds rows x H) are checked only by moe_tail_create, so
+ * an OK here is necessary, not sufficient: create's answer is final.
+ * cfg is read and not kept. */
 moe_tail_status moe_tail_check_config(const moe_tail_config* cfg);
 
-/* Create a handle: validates cfg, checks the device is gfx950, allocates the
- * handle-owned scratch (exchange buffers, counters, error word) sized for
- * max_rows, and zeroes it.  On failure *out is NULL. */
+/* Create a handle: validates cfg, checks the device is gfx950 and that one
+ * workgroup of the persistent kernel fits on every compute unit (all of them
+ * must be resident at once), allocates the handle-owned scratch (exchange
+ * buffers, counters, error word) sized for max_rows, and zeroes it.  The
+ * handle owns that scratch; the caller's tensors are never copied.  On
+ * failure *out is NULL and moe_tail_strerror(NULL) holds the reason:
+ * EINVAL (cfg), EUNSUPPORTED (not gfx950; H or LDS beyond this device),
+ * ENOMEM, EHIP.  Source: "[AMD] integrate kimi k3 monokernel", K2 commit text,
+ * section Modifications (one scratch buffer for each width; the launch reads
+ * the serving engine's weights in place and makes no weight copies). */
 moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
 
 /* Enqueue one call on `stream` (a hipStream_t; NULL = default stream) and
- * return without synchronising.  1 <= rows <= max_rows.  One launch takes up
+ * return without synchronising.  The call is the whole tail in one persistent
+ * launch ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation:
+ * the layer tail as a single launch; Kernel checks: graph replays of mixed
+ * widths give the eager bits).  1 <= rows <= max_rows.  One launch takes up
  * to 16 rows (its MFMA columns); more rows (MTP verify batches) run as
  * ceil(rows / 16) launches over balanced row ranges, in order on the stream,
  * each de-duplicating and streaming its own experts.  Graph-capturable:
@@ -161,7 +177,9 @@ moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
 moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_tail_args* args, void* stream);
 
 /* Read and clear the sticky device error word (MOE_TAIL_OK or
- * MOE_TAIL_ETIMEOUT).  Synchronises the device first.  While the word is set,
+ * MOE_TAIL_ETIMEOUT).  Every cross-workgroup wait has a deadline, and a wait
+ * that passes it stops the whole launch ("[AMD] integrate kimi k3 monokernel",
+ * K2 commit text, Motivation, and the fault row of Kernel checks).  Synchronises the device first.  While the word is set,
  * later calls on the handle give up at their first wait that is not already
  * satisfied (their outputs are then undefined); reading an error also resets
  * the handle's call epochs and counters, so the next call starts clean. */

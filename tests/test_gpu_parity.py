@@ -115,11 +115,13 @@ def _grouped_rows(cfg, w, max_attempts=64):
 
 
 @pytest.mark.parametrize("name,rows,n_group,topk_group,scale", [
-    ("c0", 2, 2, 1, 1.0), ("c1", 8, 8, 3, 1.0), ("c3", 4, 8, 4, 2.5)])
+    ("c0", 2, 2, 1, 1.0), ("c1", 8, 8, 3, 1.0), ("c3", 4, 8, 4, 2.5), ("c4", 16, 8, 4, 1.0)])
 def test_parity_grouped_routing_and_routed_scale(name, rows, n_group, topk_group, scale):
     """Group-limited top-k and a routed scaling factor on the GPU against the
     oracle: one lane per group (c0), 8 lanes per group with softmax keys (c1
-    at 8 rows), sigmoid keys with a selection bias and a scale of 2.5 (c3)."""
+    at 8 rows), sigmoid keys with a selection bias and a scale of 2.5 (c3),
+    and 6 lanes per group, not a power of two (c4's 384 experts in 8 groups
+    at 16 rows)."""
     import dataclasses
 
     cfg = dataclasses.replace(synth.CONFIGS[name].with_rows(rows), n_group=n_group, topk_group=topk_group,
@@ -134,6 +136,31 @@ def test_parity_grouped_routing_and_routed_scale(name, rows, n_group, topk_group
     check_against_oracle(g, o, cfg)
     gs = cfg.experts // n_group
     for row in range(rows):
+        assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
+
+
+@pytest.mark.parametrize("experts,n_group,topk_group,topk", [
+    (192, 8, 3, 6), (320, 8, 2, 8), (384, 4, 2, 8), (64, 4, 2, 4), (96, 4, 1, 3)])
+def test_parity_grouped_routing_any_group_width(experts, n_group, topk_group, topk):
+    """Group-limited routing where a group spans a number of 8-expert lanes
+    that is not a power of two (3, 5, 12 lanes) or is small (2, 3 lanes):
+    every group's two largest keys must be found inside the group only."""
+    import dataclasses
+
+    from gpu_harness import dev
+
+    cfg = dataclasses.replace(synth.Config("grp%d" % experts, 30 + experts % 97, 4, 1024, experts, topk, 64, 64),
+                              n_group=n_group, topk_group=topk_group)
+    _say("grouped width", experts, n_group, topk_group, topk)
+    w = synth.make_weights(cfg)
+    x, r = _grouped_rows(cfg, w)
+    o = oracle.moe_tail(x, r, w, cfg)
+    h = handle_for(cfg)
+    g = run(h, cfg, {k: dev(v) for k, v in w.items()}, x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    gs = experts // n_group
+    for row in range(cfg.rows):
         assert len({int(e) // gs for e in g["ids"][row]}) <= topk_group
 
 
