@@ -176,7 +176,10 @@ void oracle_topk(int E, int K, const double* keys, int32_t* ids) {
 }
 
 /* Normalised top-K weights. */
-/* Group-limited top-K: the E experts form n_group groups of E / n_group
+/* Group-limited top-K (parity unpinned with respect to the pages: the pages
+ * do not describe group-limited routing; this rule is the build's own reading
+ * of a routing variant, checked only against its own definition and special
+ * cases).  The E experts form n_group groups of E / n_group
  * consecutive ids.  A group's score is the sum of its two largest keys (its
  * one key when a group has a single expert).  The topk_group groups with the
  * largest scores are kept (equal scores: the lower group first), and the
