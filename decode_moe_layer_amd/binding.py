@@ -22,7 +22,8 @@ DEBUG_STALL_ONCE = 2
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EHIP", 5: "ETIMEOUT"}
 
 EXPORTS = ("moe_tail_check_config", "moe_tail_create", "moe_tail_run", "moe_tail_get_error",
-           "moe_tail_strerror", "moe_tail_destroy")
+           "moe_tail_strerror", "moe_tail_destroy", "moe_tail_run_noalloc")
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class Config(ctypes.Structure):
@@ -82,6 +83,8 @@ def lib():
         L.moe_tail_strerror.argtypes = [vp]
         L.moe_tail_destroy.restype = None
         L.moe_tail_destroy.argtypes = [vp]
+        L.moe_tail_run_noalloc.restype = ctypes.c_int
+        L.moe_tail_run_noalloc.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.POINTER(Args), vp]
         _lib = L
     return _lib
 
@@ -101,6 +104,31 @@ def check_config(cfg: Config) -> int:
 def strerror(handle=None) -> str:
     s = lib().moe_tail_strerror(handle)
     return s.decode() if s else ""
+
+
+def _args(x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13, ws2, out, res_out=None,
+          topk_ids=None, topk_w=None, dbg_logits=None, dbg_y_routed=None, dbg_y_shared=None, shared_gate=None,
+          attn=None, w_o=None):
+    return Args(*[_ptr(t) for t in (x, residual, gamma, router_w, router_bias, w13_q, w13_s, w2_q, w2_s, ws13, ws2,
+                                    out, res_out, topk_ids, topk_w, dbg_logits, dbg_y_routed, dbg_y_shared,
+                                    shared_gate, attn, w_o)])
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    return stream
+
+
+def run_noalloc(cfg: Config, rows, *tensors, stream=None, **kw):
+    """moe_tail_run_noalloc: one call with no handle (the library's static scratch); same
+    tensor arguments as MoeTail.run."""
+    a = _args(*tensors, **kw)
+    st = lib().moe_tail_run_noalloc(ctypes.byref(cfg), rows, ctypes.byref(a), ctypes.c_void_p(_stream(stream)))
+    if st != OK:
+        raise MoeTailError(st, strerror(None))
 
 
 def _ptr(t):

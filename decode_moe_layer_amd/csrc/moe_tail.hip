@@ -57,6 +57,7 @@
 // an activation poll is checked).
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <vector>
 #include <math.h>
 #include <stdarg.h>
@@ -135,6 +136,7 @@ struct Params {
   unsigned long long deadline_ticks;
   uint32_t debug_flags;
   int debug_block;
+  int sticky;  // an unread earlier timeout makes this call give up at its first unmet wait
   const uint16_t* x;
   const uint16_t* res;
   const uint16_t* gamma;
@@ -379,7 +381,7 @@ __device__ __forceinline__ bool give_up(const Params& p, Bank* bk, unsigned long
   const int lane = threadIdx.x & 63;
   uint32_t ab = 0;
   if (lane == 0) ab = __hip_atomic_load(&bk->abort_[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 1) ab = __hip_atomic_load(&p.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 1 && p.sticky) ab = __hip_atomic_load(&p.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (__ballot(ab != 0u)) return true;
   if (wall_clock64() - t0 > p.deadline_ticks) {
     if (lane == 0) {
@@ -1692,6 +1694,7 @@ struct moe_tail {
   uint16_t* a_r;
   int S1, TC, n_rb, n_sb, Ep;
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
+  int sticky;       // 1: an unread timeout makes later calls give up at once (handles); 0: each call starts clean
   int max_rows_call;  // the caller's max_rows (cfg.max_rows is the per-launch one, at most MAX_R)
   uint16_t* xbuf;     // [max_rows_call, H] bf16: x computed by the out_proj front (attn_dim > 0)
   char err[256];
@@ -1753,131 +1756,177 @@ extern "C" moe_tail_status moe_tail_check_config(const moe_tail_config* c) {
     if (e_ != hipSuccess) return fail((h), MOE_TAIL_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
-extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out) {
-  if (!out) return fail(nullptr, MOE_TAIL_EINVAL, "out is NULL");
-  *out = nullptr;
-  moe_tail_status st = moe_tail_check_config(cfg);
-  if (st != MOE_TAIL_OK) return st;
-  // everything below is sized per launch: at most MAX_R rows
-  const int max_rows_call = cfg->max_rows;
-  moe_tail_config icfg = *cfg;
-  if (icfg.max_rows > mt::MAX_R) icfg.max_rows = mt::MAX_R;
-  cfg = &icfg;
-  int dev = cfg->device;
-  if (dev < 0) HIPCHK(nullptr, hipGetDevice(&dev));
+// What a handle needs to know of its device.
+struct DevInfo {
+  int G;                 // compute units = workgroups per launch
+  size_t lds_per_block;  // bytes of LDS a workgroup may use
+  int wclk_khz;          // wall-clock (s_memrealtime) rate
+};
+
+static moe_tail_status dev_info(int dev, DevInfo* di) {
   hipDeviceProp_t prop;
   HIPCHK(nullptr, hipGetDeviceProperties(&prop, dev));
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
-  const int G = prop.multiProcessorCount;
+  di->G = prop.multiProcessorCount;
+  if (di->G > mt::MAX_G) return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d compute units, at most %d supported", di->G, mt::MAX_G);
+  di->lds_per_block = (size_t)prop.sharedMemPerBlock;
+  int wclk_khz = 0;
+  HIPCHK(nullptr, hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, dev));
+  di->wclk_khz = wclk_khz > 0 ? wclk_khz : 100000;
+  return MOE_TAIL_OK;
+}
+
+// Byte offsets of the scratch regions (each 256-byte aligned).
+struct ScratchLayout {
+  size_t o_ctl, o_xn, o_xnt, o_lg, o_pt, o_gp, o_rs, o_as, o_ar, o_xb, total;
+};
+
+// Every kernel of the tail, in the order: xn staged in LDS (8), xn from global scratch (4).
+static const void* const k_all[12] = {
+    (const void*)mt::moe_tail_kernel_lds,    (const void*)mt::moe_tail_kernel_lds_rs,
+    (const void*)mt::moe_tail_kernel_lds_f,  (const void*)mt::moe_tail_kernel_lds_rs_f,
+    (const void*)mt::moe_tail_kernel_lds_8,  (const void*)mt::moe_tail_kernel_lds_rs_8,
+    (const void*)mt::moe_tail_kernel_lds_f8, (const void*)mt::moe_tail_kernel_lds_rs_f8,
+    (const void*)mt::moe_tail_kernel_gm,     (const void*)mt::moe_tail_kernel_gm_f,
+    (const void*)mt::moe_tail_kernel_gm_8,   (const void*)mt::moe_tail_kernel_gm_f8};
+
+// Fill every field of h that depends only on the configuration and the device
+// (no allocation, no pointer into scratch yet) and the scratch layout it needs.
+static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const DevInfo& di, moe_tail_t* h,
+                                   ScratchLayout* L) {
+  moe_tail_status st = moe_tail_check_config(cfg_in);
+  if (st != MOE_TAIL_OK) return st;
+  // everything below is sized per launch: at most MAX_R rows
+  moe_tail_config icfg = *cfg_in;
+  if (icfg.max_rows > mt::MAX_R) icfg.max_rows = mt::MAX_R;
+  const moe_tail_config* cfg = &icfg;
+  const int G = di.G;
   hipFuncAttributes fa;
   HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel_lds));
-  if (G > mt::MAX_G) return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d compute units, at most %d supported", G, mt::MAX_G);
   const int S1 = chunks_per_block(cfg->hidden, cfg->num_experts, G), TC = cfg->hidden / 32 / S1;
   const int n_rb = (cfg->num_experts + 15) / 16, n_sb = cfg->shared_inter / 8;
   const int n_it = (n_rb + n_sb) * S1;
   if ((n_it + G - 1) / G > mt::MAX_ITEMS1)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d router/shared items exceed %d per workgroup", n_it, mt::MAX_ITEMS1);
-  const LdsPlan plan = lds_plan(cfg, G, TC, fa.sharedSizeBytes, (size_t)prop.sharedMemPerBlock);
-  const size_t dyn = plan.dyn;
-  if (dyn + fa.sharedSizeBytes > (size_t)prop.sharedMemPerBlock)
-    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", dyn + fa.sharedSizeBytes,
-                (size_t)prop.sharedMemPerBlock);
+  const LdsPlan plan = lds_plan(cfg, G, TC, fa.sharedSizeBytes, di.lds_per_block);
+  if (plan.dyn + fa.sharedSizeBytes > di.lds_per_block)
+    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", plan.dyn + fa.sharedSizeBytes,
+                di.lds_per_block);
   if ((cfg->hidden + G - 1) / G > 16 * mt::MAX_BLK)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "hidden %d too large for %d workgroups", cfg->hidden, G);
-  int wclk_khz = 0;
-  HIPCHK(nullptr, hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, dev));
-  if (wclk_khz <= 0) wclk_khz = 100000;
-
-  moe_tail_t* h = (moe_tail_t*)calloc(1, sizeof(moe_tail_t));
-  if (!h) return fail(nullptr, MOE_TAIL_ENOMEM, "host allocation failed");
+  memset(h, 0, sizeof(*h));
   h->cfg = *cfg;
-  h->max_rows_call = max_rows_call;
+  h->max_rows_call = cfg_in->max_rows;
   h->device = dev;
   h->G = G;
-  h->lds_dyn = dyn;
+  h->lds_dyn = plan.dyn;
   h->plan = plan;
   const unsigned long long us = cfg->deadline_us ? cfg->deadline_us : 200000u;
-  h->deadline_ticks = us * (unsigned long long)wclk_khz / 1000ull;
+  h->deadline_ticks = us * (unsigned long long)di.wclk_khz / 1000ull;
   h->S1 = S1;
   h->TC = TC;
   h->n_rb = n_rb;
   h->n_sb = n_sb;
   h->Ep = (cfg->num_experts + 7) & ~7;
-
-  const size_t R = cfg->max_rows, H = cfg->hidden, E = cfg->num_experts, K = cfg->top_k;
+  h->sticky = 1;
+  const size_t R = cfg->max_rows, H = cfg->hidden, K = cfg->top_k;
   const size_t I = cfg->inter, Is = cfg->shared_inter;
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
-  const size_t o_ctl = 0, o_xn = o_ctl + al(sizeof(mt::Ctl)), o_xnt = o_xn + al(R * H * 2);
-  const size_t o_lg = o_xnt + al(R * H * 4), o_pt = o_lg + al(R * (size_t)h->Ep * 8);
-  const size_t o_gp = o_pt + al((size_t)n_it * 2048), o_rs = o_gp + al(R * mt::NQ * 8), o_as = o_rs + al(R * 8);
-  const size_t o_ar = o_as + al(R * (Is ? Is : 1) * 2), o_xb = o_ar + al(R * K * I * 2);
-  const size_t total = o_xb + (cfg->attn_dim > 0 ? al((size_t)max_rows_call * H * 2) : 0);
-  (void)E;
+  L->o_ctl = 0;
+  L->o_xn = L->o_ctl + al(sizeof(mt::Ctl));
+  L->o_xnt = L->o_xn + al(R * H * 2);
+  L->o_lg = L->o_xnt + al(R * H * 4);
+  L->o_pt = L->o_lg + al(R * (size_t)h->Ep * 8);
+  L->o_gp = L->o_pt + al((size_t)n_it * 2048);
+  L->o_rs = L->o_gp + al(R * mt::NQ * 8);
+  L->o_as = L->o_rs + al(R * 8);
+  L->o_ar = L->o_as + al(R * (Is ? Is : 1) * 2);
+  L->o_xb = L->o_ar + al(R * K * I * 2);
+  L->total = L->o_xb + (cfg->attn_dim > 0 ? al((size_t)h->max_rows_call * H * 2) : 0);
+  snprintf(h->err, sizeof(h->err), "no error");
+  return MOE_TAIL_OK;
+}
+
+// Point the handle's regions into scratch memory that starts at base.
+static void place_scratch(moe_tail_t* h, const ScratchLayout& L, void* base_) {
+  char* base = (char*)base_;
+  h->scratch = base_;
+  h->scratch_bytes = L.total;
+  h->ctl = (mt::Ctl*)(base + L.o_ctl);
+  h->xn = (uint16_t*)(base + L.o_xn);
+  h->xnt = (uint64_t*)(base + L.o_xnt);
+  h->lgt = (uint64_t*)(base + L.o_lg);
+  h->part1 = (uint64_t*)(base + L.o_pt);
+  h->gpart = (uint64_t*)(base + L.o_gp);
+  h->rstdt = (uint64_t*)(base + L.o_rs);
+  h->a_s = (uint16_t*)(base + L.o_as);
+  h->a_r = (uint16_t*)(base + L.o_ar);
+  h->xbuf = h->cfg.attn_dim > 0 ? (uint16_t*)(base + L.o_xb) : nullptr;
+}
+
+// Let every kernel use all the LDS a workgroup may have (a launch then asks
+// for its own dynamic size; handles of different sizes never narrow each
+// other's limit), and check that one workgroup of each kernel this handle
+// may launch fits on a compute unit at the handle's dynamic LDS size: every
+// cross-workgroup wait assumes that all G workgroups are resident at once
+// (one per compute unit), which a plain launch relies on.  Call with the
+// handle's device current.
+static moe_tail_status prepare_kernels(const moe_tail_t* h, const DevInfo& di) {
+  for (int k = 0; k < 12; ++k) {
+    hipFuncAttributes fa;
+    HIPCHK(nullptr, hipFuncGetAttributes(&fa, k_all[k]));
+    const int lim = (int)(di.lds_per_block - fa.sharedSizeBytes);
+    HIPCHK(nullptr, hipFuncSetAttribute(k_all[k], hipFuncAttributeMaxDynamicSharedMemorySize, lim));
+  }
+  const bool xl = h->plan.xn_lds;
+  for (int k = xl ? 0 : 8; k < (xl ? 8 : 12); ++k) {
+    int nb = 0;
+    HIPCHK(nullptr, hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_all[k], mt::NT, h->lds_dyn));
+    if (nb < 1)
+      return fail(nullptr, MOE_TAIL_EUNSUPPORTED,
+                  "a workgroup of %d threads with %zu B of dynamic LDS does not fit on a compute unit", mt::NT,
+                  h->lds_dyn);
+  }
+  return MOE_TAIL_OK;
+}
+
+extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out) {
+  if (!out) return fail(nullptr, MOE_TAIL_EINVAL, "out is NULL");
+  *out = nullptr;
+  moe_tail_status st = moe_tail_check_config(cfg);
+  if (st != MOE_TAIL_OK) return st;
+  int dev = cfg->device;
+  if (dev < 0) HIPCHK(nullptr, hipGetDevice(&dev));
+  DevInfo di;
+  if ((st = dev_info(dev, &di)) != MOE_TAIL_OK) return st;
+  moe_tail_t* h = (moe_tail_t*)calloc(1, sizeof(moe_tail_t));
+  if (!h) return fail(nullptr, MOE_TAIL_ENOMEM, "host allocation failed");
+  ScratchLayout L;
+  if ((st = plan_handle(cfg, dev, di, h, &L)) != MOE_TAIL_OK) {
+    free(h);
+    return st;
+  }
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(dev);
-  hipError_t e = hipMalloc(&h->scratch, total);
+  void* base = nullptr;
+  hipError_t e = hipMalloc(&base, L.total);
   if (e != hipSuccess) {
     (void)hipSetDevice(prev);
     free(h);
-    return fail(nullptr, MOE_TAIL_ENOMEM, "hipMalloc(%zu): %s", total, hipGetErrorString(e));
+    return fail(nullptr, MOE_TAIL_ENOMEM, "hipMalloc(%zu): %s", L.total, hipGetErrorString(e));
   }
-  e = hipMemset(h->scratch, 0, total);
-  {
-    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds,     (const void*)mt::moe_tail_kernel_lds_rs,
-                        (const void*)mt::moe_tail_kernel_lds_f,   (const void*)mt::moe_tail_kernel_lds_rs_f,
-                        (const void*)mt::moe_tail_kernel_lds_8,   (const void*)mt::moe_tail_kernel_lds_rs_8,
-                        (const void*)mt::moe_tail_kernel_lds_f8,  (const void*)mt::moe_tail_kernel_lds_rs_f8,
-                        (const void*)mt::moe_tail_kernel_gm,      (const void*)mt::moe_tail_kernel_gm_f,
-                        (const void*)mt::moe_tail_kernel_gm_8,    (const void*)mt::moe_tail_kernel_gm_f8};
-    for (int k = plan.xn_lds ? 0 : 8; k < (plan.xn_lds ? 8 : 12) && e == hipSuccess; ++k)
-      e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-  }
-  // Every cross-workgroup wait assumes that all G workgroups are resident at
-  // once (one per compute unit); a plain launch relies on it, so each kernel
-  // this handle may launch must fit one workgroup per compute unit with its
-  // LDS, registers and waves.
-  int occ_min = 1 << 30;
-  {
-    const void* ks[] = {(const void*)mt::moe_tail_kernel_lds,     (const void*)mt::moe_tail_kernel_lds_rs,
-                        (const void*)mt::moe_tail_kernel_lds_f,   (const void*)mt::moe_tail_kernel_lds_rs_f,
-                        (const void*)mt::moe_tail_kernel_lds_8,   (const void*)mt::moe_tail_kernel_lds_rs_8,
-                        (const void*)mt::moe_tail_kernel_lds_f8,  (const void*)mt::moe_tail_kernel_lds_rs_f8,
-                        (const void*)mt::moe_tail_kernel_gm,      (const void*)mt::moe_tail_kernel_gm_f,
-                        (const void*)mt::moe_tail_kernel_gm_8,    (const void*)mt::moe_tail_kernel_gm_f8};
-    for (int k = plan.xn_lds ? 0 : 8; k < (plan.xn_lds ? 8 : 12) && e == hipSuccess; ++k) {
-      int nb = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ks[k], mt::NT, dyn);
-      occ_min = nb < occ_min ? nb : occ_min;
-    }
-  }
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  place_scratch(h, L, base);
+  e = hipMemset(base, 0, L.total);
+  if (e == hipSuccess) st = prepare_kernels(h, di);
+  if (e == hipSuccess && st == MOE_TAIL_OK) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
-  if (e != hipSuccess) {
-    (void)hipFree(h->scratch);
+  if (e != hipSuccess || st != MOE_TAIL_OK) {
+    (void)hipFree(base);
     free(h);
-    return fail(nullptr, MOE_TAIL_EHIP, "scratch setup: %s", hipGetErrorString(e));
+    return e != hipSuccess ? fail(nullptr, MOE_TAIL_EHIP, "scratch setup: %s", hipGetErrorString(e)) : st;
   }
-  if (occ_min < 1) {
-    (void)hipFree(h->scratch);
-    free(h);
-    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "a workgroup of %d threads with %zu B of dynamic LDS does not fit on a compute unit",
-                mt::NT, dyn);
-  }
-  char* base = (char*)h->scratch;
-  h->ctl = (mt::Ctl*)(base + o_ctl);
-  h->xn = (uint16_t*)(base + o_xn);
-  h->xnt = (uint64_t*)(base + o_xnt);
-  h->lgt = (uint64_t*)(base + o_lg);
-  h->part1 = (uint64_t*)(base + o_pt);
-  h->gpart = (uint64_t*)(base + o_gp);
-  h->rstdt = (uint64_t*)(base + o_rs);
-  h->scratch_bytes = total;
-  h->a_s = (uint16_t*)(base + o_as);
-  h->a_r = (uint16_t*)(base + o_ar);
-  h->xbuf = cfg->attn_dim > 0 ? (uint16_t*)(base + o_xb) : nullptr;
-  snprintf(h->err, sizeof(h->err), "no error");
   *out = h;
   return MOE_TAIL_OK;
 }
@@ -1950,6 +1999,7 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
     h->stall_spent = 1;
   }
   p.debug_block = c.debug_block;
+  p.sticky = h->sticky;
   p.x = (const uint16_t*)a->x;
   p.res = (const uint16_t*)a->residual;
   p.gamma = (const uint16_t*)a->gamma;
@@ -2073,6 +2123,69 @@ extern "C" moe_tail_status moe_tail_get_error(moe_tail_t* h) {
                 "workgroup epochs now %u..%u)",
                 w[1] < 4 ? names[w[1]] : "?", w[2], w[3], w[4], w[5], w[6], ep_lo, ep_hi);
   return MOE_TAIL_OK;
+}
+
+// ------------------------------------------------ the no-allocation entry --
+
+// Scratch of moe_tail_run_noalloc: one array per device, zero when the code
+// object loads, kept for the life of the process.  Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in for
+// the symbol): it uses the device address that hipGetSymbolAddress returns
+// for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_TAIL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEV = 64;
+struct NoallocDev {
+  int ready;         // ptr and info are valid
+  void* ptr;         // this device's address of `scratch`
+  DevInfo info;
+  size_t lds_ready;  // largest dynamic LDS size prepared so far, per kernel family (0: none)
+  size_t lds_ready_gm;
+};
+NoallocDev g_noalloc[NOALLOC_MAX_DEV];
+std::mutex g_noalloc_mu;
+}  // namespace
+
+extern "C" moe_tail_status moe_tail_run_noalloc(const moe_tail_config* cfg, int32_t rows, const moe_tail_args* a,
+                                                void* stream) {
+  moe_tail_status st = moe_tail_check_config(cfg);
+  if (st != MOE_TAIL_OK) return st;
+  if (cfg->debug_flags & MOE_TAIL_DEBUG_STALL_ONCE)
+    return fail(nullptr, MOE_TAIL_EINVAL, "MOE_TAIL_DEBUG_STALL_ONCE needs a handle");
+  int dev = 0;
+  HIPCHK(nullptr, hipGetDevice(&dev));
+  if (cfg->device >= 0 && cfg->device != dev)
+    return fail(nullptr, MOE_TAIL_EINVAL, "config device %d is not the current device %d", cfg->device, dev);
+  if (dev >= NOALLOC_MAX_DEV) return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "device %d beyond %d", dev, NOALLOC_MAX_DEV);
+  moe_tail_t h;  // a handle on the stack over the static scratch; nothing is allocated
+  ScratchLayout L;
+  {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoallocDev& d = g_noalloc[dev];
+    if (!d.ready) {  // once per device, with that device current
+      void* ptr = nullptr;
+      HIPCHK(nullptr, hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+      if ((st = dev_info(dev, &d.info)) != MOE_TAIL_OK) return st;
+      d.ptr = ptr;
+      d.ready = 1;
+    }
+    if ((st = plan_handle(cfg, dev, d.info, &h, &L)) != MOE_TAIL_OK) return st;
+    if (L.total > sizeof(scratch))
+      return fail(nullptr, MOE_TAIL_EINVAL, "this configuration needs %zu B of scratch; moe_tail_run_noalloc has %zu",
+                  L.total, sizeof(scratch));
+    // the residency check passed at this dynamic LDS size or a larger one
+    size_t& done = h.plan.xn_lds ? d.lds_ready : d.lds_ready_gm;
+    if (h.lds_dyn > done || !done) {
+      if ((st = prepare_kernels(&h, d.info)) != MOE_TAIL_OK) return st;
+      done = h.lds_dyn > done ? h.lds_dyn : done;
+    }
+    place_scratch(&h, L, d.ptr);
+  }
+  h.sticky = 0;  // nothing reads this scratch's error word: each call starts clean
+  st = moe_tail_run(&h, rows, a, stream);
+  if (st != MOE_TAIL_OK) snprintf(g_create_err, sizeof(g_create_err), "%s", h.err);
+  return st;
 }
 
 #ifdef MOE_TAIL_TIMELINE

@@ -193,6 +193,36 @@ const char* moe_tail_strerror(moe_tail_t* h);
  * still in flight. */
 void moe_tail_destroy(moe_tail_t* h);
 
+/* Scratch bytes available to moe_tail_run_noalloc (4 MiB): enough for every
+ * configuration up to 16 rows per launch with H <= 8192, E <= 512, K <= 10,
+ * I <= 256 and Is <= 512 (at most 3.3 MB); larger ones are refused. */
+#define MOE_TAIL_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Enqueues
+ * one call like moe_tail_run, without a handle: the call's scratch (exchange
+ * buffers, counters, epochs, error word) is a file-scope device array of
+ * MOE_TAIL_NOALLOC_SCRATCH_BYTES on the current device, kept for the life of
+ * the process; nothing is allocated, on the device or the host, and nothing
+ * is copied.  cfg is validated as by moe_tail_create (device must be -1 or
+ * the current device; MOE_TAIL_DEBUG_STALL_ONCE is refused), the other
+ * arguments as by moe_tail_run; a configuration whose scratch would exceed
+ * the array is refused with MOE_TAIL_EINVAL.  Errors are returned
+ * synchronously, with the text in moe_tail_strerror(NULL).  The first call on
+ * a device looks up the array's address on that device, once.
+ *
+ * Every call on a device shares that device's array and leaves its contents
+ * for the next one (each call's words are tagged with per-workgroup call
+ * counts that only grow, and each call clears the counters of the next), so
+ * successive calls may change the configuration, the rows and the pointers.
+ * Calls on one device must be ordered (one stream at a time): calls that
+ * overlap on a device race on the array, with each other and with nothing
+ * else (handles have scratch of their own).  A device-side deadline aborts
+ * that call only (its outputs are undefined) and is not reported: the next
+ * call starts clean.  Callers that need the report use a handle. */
+moe_tail_status moe_tail_run_noalloc(const moe_tail_config* cfg, int32_t rows, const moe_tail_args* args,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,3 +108,17 @@ def test_create_without_gpu_reports_error():
     with pytest.raises(binding.MoeTailError) as ei:
         binding.MoeTail(good())
     assert ei.value.status in (binding.EHIP, binding.EUNSUPPORTED)
+
+
+def test_noalloc_entry_refuses_bad_configs_on_the_host():
+    """moe_tail_run_noalloc validates its config before any GPU call: a bad
+    field and the handle-only stall flag are refused synchronously."""
+    c = good()
+    c.hidden = 100
+    a = binding.Args()
+    assert binding.lib().moe_tail_run_noalloc(ctypes.byref(c), 1, ctypes.byref(a), None) == binding.EINVAL
+    assert "hidden" in binding.strerror(None)
+    c = good()
+    c.debug_flags = binding.DEBUG_STALL_ONCE
+    assert binding.lib().moe_tail_run_noalloc(ctypes.byref(c), 1, ctypes.byref(a), None) == binding.EINVAL
+    assert "handle" in binding.strerror(None)
