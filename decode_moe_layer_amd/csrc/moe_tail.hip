@@ -85,6 +85,9 @@ constexpr int MAX_BLK = 2;            // 16-row down blocks per workgroup
 constexpr int D_BF = 12;              // bf16 weight loads in flight per wave
 constexpr int D_FP4_G = 4;            // MXFP4 items in flight per wave when activations come from global memory
 constexpr int XPAD = 8;               // bf16 padding per LDS activation row
+constexpr int FRONT_AC = 1024;                       // out_proj front: attention columns per K chunk
+constexpr int FRONT_WV = FRONT_AC / 8 / 16;          // its weight vectors per thread and chunk
+constexpr int FRONT_AV = MAX_R * FRONT_AC / 8 / NT;  // its attention vectors per thread and chunk (staged in LDS)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -151,6 +154,10 @@ struct Params {
   const uint16_t* ws13;
   const uint16_t* ws2;
   const uint16_t* sgate;  // [H] shared-expert gate, or null
+  const uint16_t* attn;   // [R][A] attention rows in place of x (the out_proj front), or null
+  const uint16_t* w_o;    // [H][A] out_proj weights (with attn)
+  int A;                  // attention width
+  int HR;                 // hidden columns per workgroup slice (even)
   uint16_t* out;
   uint16_t* res_out;
   int32_t* topk_ids;
@@ -165,6 +172,7 @@ struct Params {
   uint64_t* part1;  // [blocks * S1][16][16] tagged fp32 K-chunk partial sums
   uint64_t* gpart;  // [R][NQ] tagged fp32 partial dots of the shared gate, one per norm slice
   uint64_t* rstdt;  // [R] tagged fp32 rstd of each row (folded norm)
+  uint64_t* xft;    // [R][H/2] tagged x pairs computed by the out_proj front, one slice per workgroup
   uint64_t* ast;  // [R][Is/2] tagged shared a, two bf16 (i, i + 1) per word
   uint64_t* art;  // [P][I/2] tagged routed a, the same way
 };
@@ -544,18 +552,20 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 
   TL(0);
   // This workgroup's output rows [h0, h0 + hn) of the combine (R hn <= NT: one
-  // element per thread).  Their x and residual are loaded now, so that the
-  // combine at the end does not wait for memory.
-  const int HR = (H + G - 1) / G;
-  const int h0 = cta * HR, hn = max(0, min(H, h0 + HR) - h0);
+  // element per thread; an even width HR).  Their x and residual are loaded
+  // now, so that the combine at the end does not wait for memory.
+  const int HR = p.HR;
+  const int h0 = min(H, cta * HR), hn = max(0, min(H, h0 + HR) - h0);
+  const bool front = FEAT && p.attn;  // attention rows in place of x: x comes from the out_proj front below
   uint32_t cx, cr;
   {
     const int r = tid / max(hn, 1), hh = tid - r * max(hn, 1);
     const uint32_t off = tid < R * hn ? (uint32_t)(r * H + h0 + hh) * 2u : OOB;
-    cx = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.x, (uint32_t)(R * H * 2)), (int)off, 0, 0);
-    // no branch around the residual's load (an empty range reads zero), so
-    // that nothing waits for either load before the weights go out
-    cr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.res ? p.res : p.x, p.res ? (uint32_t)(R * H * 2) : 0u), (int)off, 0, 0);
+    // no branches around these loads (an empty range reads zero), so that
+    // nothing waits for them before the weights go out
+    cx = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.x, p.x ? (uint32_t)(R * H * 2) : 0u), (int)off, 0, 0);
+    cr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.res ? p.res : p.gamma, p.res ? (uint32_t)(R * H * 2) : 0u),
+                                              (int)off, 0, 0);
   }
   TL(30);
   // ---- call epoch: every workgroup counts the calls it has started, so all
@@ -635,6 +645,98 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         for (int k = 0; k < FCH; ++k) fold_load(tid + k * NT, fx[k], fr[k], fg[k]);
     }
   };
+  // ---- the out_proj front (attention rows in place of x): every workgroup
+  // computes x of its slice, x[r][h] = bf16(sum_a attn[r][a] w_o[h][a]), and
+  // publishes it as tagged pairs before its weights go out; the norm
+  // workgroups read whole rows of it.  Every bf16 product is exact in double
+  // and the sum is taken in double (thread (fh, fp) sums columns a = 8 (fp +
+  // 16 j) .. + 7 of each K chunk for hidden row h0 + fh, then the 16 lanes of
+  // a row in a fixed order), rounded to bf16 once, as the projection's
+  // definition asks ("[AMD] integrate kimi k3 monokernel", K2 commit text,
+  // Motivation and Modifications: out_proj in the same launch as the tail).
+  if constexpr (FEAT) {
+    if (front) {
+      const int fh = tid >> 4, fpart = tid & 15, A = p.A;
+      const rsrc_t rfa = make_rsrc(p.attn, (uint32_t)(R * A * 2));
+      const rsrc_t rfw = make_rsrc(p.w_o, (uint32_t)((size_t)H * A * 2));
+      uint16_t* const at = (uint16_t*)dyn;                      // [R][FRONT_AC] a K chunk of the attention rows
+      uint16_t* const sx = (uint16_t*)&S.red[0][0][0];         // [R][32] this slice's x (tiles idle until later)
+      double acc[MAX_R];
+#pragma unroll
+      for (int r = 0; r < MAX_R; ++r) acc[r] = 0.0;
+      u32x4 fav[FRONT_AV], fwv[FRONT_WV];
+      auto front_load = [&](int a0) {
+        const int ac = min(FRONT_AC, A - a0), n8 = R * (ac / 8);
+#pragma unroll
+        for (int k = 0; k < FRONT_AV; ++k) {
+          const int q = tid + k * NT, r = q / (ac / 8), c8 = q - r * (ac / 8);
+          fav[k] = ld16<0>(rfa, q < n8 ? (uint32_t)(r * A + a0 + c8 * 8) * 2u : OOB);
+        }
+#pragma unroll
+        for (int j = 0; j < FRONT_WV; ++j) {
+          const int c8 = fpart + 16 * j;
+          fwv[j] = ld16<0>(rfw, c8 * 8 < ac && fh < hn ? (uint32_t)((size_t)(h0 + fh) * A + a0 + c8 * 8) * 2u : OOB);
+        }
+      };
+      front_load(0);
+      for (int a0 = 0; a0 < A; a0 += FRONT_AC) {
+        const int ac = min(FRONT_AC, A - a0), n8 = R * (ac / 8);
+        if (a0) {
+          __syncthreads();  // the previous chunk's readers are done
+          front_load(a0);
+        }
+#pragma unroll
+        for (int k = 0; k < FRONT_AV; ++k) {
+          const int q = tid + k * NT, r = q / (ac / 8), c8 = q - r * (ac / 8);
+          if (q < n8) *(u32x4*)(at + r * FRONT_AC + c8 * 8) = fav[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < FRONT_WV; ++j) {
+          const int c8 = fpart + 16 * j;
+          if (c8 * 8 < ac && fh < hn) {
+            double wd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              wd[2 * e] = (double)bf2f(fwv[j][e] & 0xFFFFu);
+              wd[2 * e + 1] = (double)bf2f(fwv[j][e] >> 16);
+            }
+#pragma unroll
+            for (int r = 0; r < MAX_R; ++r) {
+              if (r < R) {
+                const u32x4 av = lds16(at + r * FRONT_AC + c8 * 8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  acc[r] = fma((double)bf2f(av[e] & 0xFFFFu), wd[2 * e], acc[r]);
+                  acc[r] = fma((double)bf2f(av[e] >> 16), wd[2 * e + 1], acc[r]);
+                }
+              }
+            }
+          }
+        }
+      }
+      // the 16 lanes of a hidden row: a prefix sum with row shifts, whose
+      // lane 15 holds the total
+#pragma unroll
+      for (int r = 0; r < MAX_R; ++r) {
+        if (r < R) {
+          double v = acc[r];
+          v += dpp_f64<0x111, 0xF>(v);
+          v += dpp_f64<0x112, 0xF>(v);
+          v += dpp_f64<0x114, 0xF>(v);
+          v += dpp_f64<0x118, 0xF>(v);
+          if (fpart == 15 && fh < hn) sx[r * 32 + fh] = (uint16_t)d2bf(v);
+        }
+      }
+      if (tid == 0) S.ep = epv + 1u;  // the tags need the epoch here
+      __syncthreads();
+      const uint32_t epf = S.ep;
+      const int r = tid / max(hn, 1), hh = tid - r * max(hn, 1);
+      if (tid < R * hn) cx = sx[r * 32 + hh];
+      const uint32_t xnext = (uint32_t)__shfl_down((int)cx, 1);  // column hh + 1 of the same row (hh even)
+      if (tid < R * hn && (hh & 1) == 0) st_tag(p.xft + ((size_t)r * H + h0 + hh) / 2, cx | (xnext << 16), epf);
+    }
+  }
   // weights do not depend on the activations: their loads go out first,
   // except in the norm workgroups, whose row loads must not queue behind them
   fold_issue();
@@ -650,15 +752,45 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // H <= 16384 = 4 x 512 x 8
       const int i = (k * NT + tid) * 8;
-      xv[k] = ld16<0>(rx, i < H ? (uint32_t)i * 2u : OOB);
+      xv[k] = ld16<0>(rx, !front && i < H ? (uint32_t)i * 2u : OOB);
       rv[k] = ld16<0>(rr, i < H ? (uint32_t)i * 2u : OOB);
     }
     // this workgroup's slice, loaded up front as well (8 elements per thread)
     const int i = q * SL + tid * 8;
     const bool sl = tid * 8 < SL;
-    const u32x4 x8 = ld16<0>(rx, sl ? (uint32_t)i * 2u : OOB);
+    u32x4 x8 = ld16<0>(rx, !front && sl ? (uint32_t)i * 2u : OOB);
     const u32x4 r8 = ld16<0>(rr, sl ? (uint32_t)i * 2u : OOB);
     const u32x4 g8 = ld16<0>(rg, sl ? (uint32_t)i * 2u : OOB);
+    if constexpr (FEAT) {
+      if (front) {  // the row's x from every workgroup's slice of the front, polled until all is this call's
+        const uint32_t epf = S.ep;
+        const rsrc_t rxf = make_rsrc(p.xft + (size_t)row * (H / 2), (uint32_t)(H * 4));
+        auto ld8 = [&](int e, bool v, bool& ok) -> u32x4 {  // 8 elements from two tagged-pair loads
+          const u32x4 a = ld_tag2(rxf, v ? (uint32_t)(e / 2) : OOB / 8u);
+          const u32x4 b = ld_tag2(rxf, v ? (uint32_t)(e / 2 + 2) : OOB / 8u);
+          ok = ok && (!v || (a[1] == epf && a[3] == epf && b[1] == epf && b[3] == epf));
+          return (u32x4){a[0], a[2], b[0], b[2]};
+        };
+        const unsigned long long t0 = wall_clock64();
+        for (;;) {
+          bool ok = true;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int e = (k * NT + tid) * 8;
+            xv[k] = ld8(e, e < H, ok);
+          }
+          x8 = ld8(i, sl, ok);
+          if (__syncthreads_and(ok && !stall)) break;
+          if (tid < 64) {
+            const bool gu = give_up(p, &p.ctl->bank[epf & 1], t0, 0, 0u, 1u, epf, 0u);
+            if (tid == 0) S.flags[6] = gu;
+          }
+          __syncthreads();
+          if (S.flags[6]) return;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
     u32x4 wg8 = {0u, 0u, 0u, 0u};  // shared gate slice
     if (FEAT && p.sgate) wg8 = ld16<0>(make_rsrc(p.sgate, (uint32_t)(H * 2)), sl ? (uint32_t)i * 2u : OOB);
     double ss = 0.0;
@@ -1261,7 +1393,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           qc = 0;
           p2_reduce(acc, u);
           acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-          if (kk < 12) TL(14 + kk);
+          if (kk < 8) TL(14 + kk);
           ++kk;
         }
       });
@@ -1317,7 +1449,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
           tt = 0;
           p2_reduce(acc, u0 + kk * G);
           acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-          if (kk < 12) TL(14 + kk);
+          if (kk < 8) TL(14 + kk);
           ++kk;
         }
       });
@@ -1620,7 +1752,7 @@ MT_KERNEL(moe_tail_kernel_lds_rs_f8, true, true, true, true)
 MT_KERNEL(moe_tail_kernel_gm_f8, false, false, true, true)
 #undef MT_KERNEL
 static const void* kernel_for(const Params& p) {
-  const bool f = p.sgate || p.n_group > 1 || p.fold;
+  const bool f = p.sgate || p.n_group > 1 || p.fold || p.attn;
   if (p.f8) {
     if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f8 : (const void*)moe_tail_kernel_gm_8;
     if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_rs_8;
@@ -1629,66 +1761,6 @@ static const void* kernel_for(const Params& p) {
   if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f : (const void*)moe_tail_kernel_gm;
   if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f : (const void*)moe_tail_kernel_lds_rs;
   return f ? (const void*)moe_tail_kernel_lds_f : (const void*)moe_tail_kernel_lds;
-}
-
-// The out_proj front: x[r][h] = bf16(sum_a attn[r][a] w_o[h][a]).  Every
-// bf16 product is exact in double and the sum is taken in double, then
-// rounded to bf16 once, as the projection's definition asks; the work is a
-// few MB of weights, so plain vector loads and fp64 FMAs are enough.  A
-// workgroup of 256 threads owns OP_H output columns h for up to MAX_R rows
-// (blockIdx.y selects the row block): thread (hi, ks) sums K elements
-// ks*8 + OP_KS*8*j .. +7 (OP_KS lanes read contiguous bytes of a weight row
-// per step, and each thread has only A / (8 OP_KS) steps of load latency),
-// and the OP_KS slices are added in order.
-constexpr int OP_NT = 256, OP_KS = 32, OP_H = OP_NT / OP_KS;
-__global__ __launch_bounds__(OP_NT) void moe_tail_out_proj_kernel(const uint16_t* attn, const uint16_t* w_o,
-                                                                   uint16_t* x, int rows, int A, int H) {
-  __shared__ double part[OP_KS][OP_H][MAX_R + 1];  // [slice][column][row]
-  const int tid = threadIdx.x, ks = tid % OP_KS, hi = tid / OP_KS;
-  const int h = blockIdx.x * OP_H + hi;
-  const int r0 = blockIdx.y * MAX_R, R = min(MAX_R, rows - r0);
-  attn += (size_t)r0 * A;
-  x += (size_t)r0 * H;
-  const rsrc_t rw = make_rsrc(w_o, (uint32_t)((size_t)H * A * 2));
-  const rsrc_t ra = make_rsrc(attn, (uint32_t)((size_t)R * A * 2));
-  double acc[MAX_R];
-#pragma unroll
-  for (int r = 0; r < MAX_R; ++r) acc[r] = 0.0;
-#pragma unroll 2
-  for (int a0 = ks * 8; a0 < A; a0 += OP_KS * 8) {
-    const u32x4 wv = ld16<0>(rw, h < H ? (uint32_t)(h * A + a0) * 2u : OOB);
-    u32x4 av[MAX_R];
-#pragma unroll
-    for (int r = 0; r < MAX_R; ++r)
-      if (r < R) av[r] = ld16<0>(ra, (uint32_t)(r * A + a0) * 2u);
-    double wd[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      wd[2 * c] = (double)bf2f(wv[c] & 0xFFFFu);
-      wd[2 * c + 1] = (double)bf2f(wv[c] >> 16);
-    }
-#pragma unroll
-    for (int r = 0; r < MAX_R; ++r) {
-      if (r < R) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[r] = fma(wd[2 * c], (double)bf2f(av[r][c] & 0xFFFFu), acc[r]);
-          acc[r] = fma(wd[2 * c + 1], (double)bf2f(av[r][c] >> 16), acc[r]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < MAX_R; ++r) part[ks][hi][r] = acc[r];
-  __syncthreads();
-  if (tid < OP_H * MAX_R) {
-    const int r = tid % MAX_R, hc = tid / MAX_R, ho = blockIdx.x * OP_H + hc;
-    if (r < R && ho < H) {
-      double sum = 0.0;
-      for (int k = 0; k < OP_KS; ++k) sum += part[k][hc][r];
-      x[(size_t)r * H + ho] = (uint16_t)d2bf(sum);
-    }
-  }
 }
 
 }  // namespace mt
@@ -1707,9 +1779,14 @@ struct LdsPlan {
 
 static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
+// Hidden columns per workgroup slice (the combine's outputs, and the out_proj
+// front's x): H over the workgroups, rounded up to an even count, so that x
+// travels in bf16 pairs that never straddle two slices.
+static int slice_width(int H, int G) { return ((H + G - 1) / G + 1) & ~1; }
+
 static LdsPlan lds_plan(const moe_tail_config* c, int G, int TC, size_t static_bytes, size_t limit) {
   LdsPlan L;
-  const size_t R = c->max_rows, P = (size_t)c->max_rows * c->top_k, HR = (size_t)(c->hidden + G - 1) / G;
+  const size_t R = c->max_rows, P = (size_t)c->max_rows * c->top_k, HR = (size_t)slice_width(c->hidden, G);
   L.xs = c->hidden + mt::XPAD;
   L.cs = TC * 32 + mt::XPAD;
   L.as = c->inter + mt::XPAD;
@@ -1720,7 +1797,10 @@ static LdsPlan lds_plan(const moe_tail_config* c, int G, int TC, size_t static_b
   L.down = L.off_shp + al16((size_t)mt::NW * R * HR * 4);
   L.xn = (R + 1) * (size_t)L.xs * 2;
   L.chunk = (R + 1) * (size_t)L.cs * 2;
-  const size_t base = L.down > L.chunk ? L.down : L.chunk;
+  // the out_proj front stages a K chunk of the attention rows first
+  const size_t fr = c->attn_dim > 0 ? R * (size_t)mt::FRONT_AC * 2 : 0;
+  size_t base = L.down > L.chunk ? L.down : L.chunk;
+  base = base > fr ? base : fr;
   L.xn_lds = static_bytes + (L.xn > base ? L.xn : base) <= limit;
   L.dyn = L.xn_lds && L.xn > base ? L.xn : base;
   return L;
@@ -1757,7 +1837,7 @@ struct moe_tail {
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
   int sticky;       // 1: an unread timeout makes later calls give up at once (handles); 0: each call starts clean
   int max_rows_call;  // the caller's max_rows (cfg.max_rows is the per-launch one, at most MAX_R)
-  uint16_t* xbuf;     // [max_rows_call, H] bf16: x computed by the out_proj front (attn_dim > 0)
+  uint64_t* xft;      // [max_rows, H/2] tagged x pairs of the out_proj front (attn_dim > 0)
   char err[256];
 };
 
@@ -1840,7 +1920,7 @@ static moe_tail_status dev_info(int dev, DevInfo* di) {
 
 // Byte offsets of the scratch regions (each 256-byte aligned).
 struct ScratchLayout {
-  size_t o_ctl, o_xn, o_xnt, o_lg, o_pt, o_gp, o_rs, o_as, o_ar, o_xb, total;
+  size_t o_ctl, o_xn, o_xnt, o_lg, o_pt, o_gp, o_rs, o_as, o_ar, o_xf, total;
 };
 
 // Every kernel of the tail, in the order: xn staged in LDS (8), xn from global scratch (4).
@@ -1874,7 +1954,7 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
   if (plan.dyn + fa.sharedSizeBytes > di.lds_per_block)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", plan.dyn + fa.sharedSizeBytes,
                 di.lds_per_block);
-  if ((cfg->hidden + G - 1) / G > 16 * mt::MAX_BLK)
+  if (slice_width(cfg->hidden, G) > 16 * mt::MAX_BLK)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "hidden %d too large for %d workgroups", cfg->hidden, G);
   memset(h, 0, sizeof(*h));
   h->cfg = *cfg;
@@ -1903,8 +1983,8 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
   L->o_rs = L->o_gp + al(R * mt::NQ * 8);
   L->o_as = L->o_rs + al(R * 8);
   L->o_ar = L->o_as + al(R * (Is ? Is : 2) * 4);
-  L->o_xb = L->o_ar + al(R * K * I * 4);
-  L->total = L->o_xb + (cfg->attn_dim > 0 ? al((size_t)h->max_rows_call * H * 2) : 0);
+  L->o_xf = L->o_ar + al(R * K * I * 4);
+  L->total = L->o_xf + (cfg->attn_dim > 0 ? al(R * H * 4) : 0);
   snprintf(h->err, sizeof(h->err), "no error");
   return MOE_TAIL_OK;
 }
@@ -1923,7 +2003,7 @@ static void place_scratch(moe_tail_t* h, const ScratchLayout& L, void* base_) {
   h->rstdt = (uint64_t*)(base + L.o_rs);
   h->ast = (uint64_t*)(base + L.o_as);
   h->art = (uint64_t*)(base + L.o_ar);
-  h->xbuf = h->cfg.attn_dim > 0 ? (uint16_t*)(base + L.o_xb) : nullptr;
+  h->xft = h->cfg.attn_dim > 0 ? (uint64_t*)(base + L.o_xf) : nullptr;
 }
 
 // Let every kernel use all the LDS a workgroup may have (a launch then asks
@@ -1998,7 +2078,8 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
   const moe_tail_config& c = h->cfg;
   if (rows < 1 || rows > c.max_rows) return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, c.max_rows);
-  const void* req[] = {a->x, a->gamma, a->router_w, a->w13_q, a->w13_s, a->w2_q, a->w2_s, a->out};
+  // x, or attention rows for the out_proj front (checked by the caller)
+  const void* req[] = {a->attn ? a->attn : a->x, a->gamma, a->router_w, a->w13_q, a->w13_s, a->w2_q, a->w2_s, a->out};
   const char* names[] = {"x", "gamma", "router_w", "w13_q", "w13_s", "w2_q", "w2_s", "out"};
   for (int k = 0; k < 8; ++k) {
     if (!req[k]) return fail(h, MOE_TAIL_EINVAL, "%s is NULL", names[k]);
@@ -2073,6 +2154,11 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.ws13 = (const uint16_t*)a->ws13;
   p.ws2 = (const uint16_t*)a->ws2;
   p.sgate = (const uint16_t*)a->shared_gate;
+  p.attn = (const uint16_t*)a->attn;
+  p.w_o = a->attn ? (const uint16_t*)a->w_o : nullptr;
+  p.A = a->attn ? c.attn_dim : 0;
+  p.HR = slice_width(c.hidden, h->G);
+  p.xft = h->xft;
   p.out = (uint16_t*)a->out;
   p.res_out = (uint16_t*)a->res_out;
   p.topk_ids = a->topk_ids;
@@ -2106,20 +2192,12 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
   if (!a) return fail(h, MOE_TAIL_EINVAL, "args is NULL");
   if (rows < 1 || rows > h->max_rows_call)
     return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, h->max_rows_call);
-  moe_tail_args fa;
-  if (a->attn) {  // the out_proj front: x = bf16(attn . w_o^T) into handle scratch, then the tail on it
+  if (a->attn) {  // the out_proj front: x = bf16(attn . w_o^T), computed in the same launch as the tail
     if (a->x) return fail(h, MOE_TAIL_EINVAL, "give x or attn, not both");
-    if (!h->xbuf) return fail(h, MOE_TAIL_EINVAL, "attn needs a handle created with attn_dim > 0");
+    if (!h->xft) return fail(h, MOE_TAIL_EINVAL, "attn needs a handle created with attn_dim > 0");
     if (!a->w_o) return fail(h, MOE_TAIL_EINVAL, "w_o is required with attn");
     if (!aligned(a->attn, 16) || !aligned(a->w_o, 16)) return fail(h, MOE_TAIL_EINVAL, "attn/w_o are not 16-byte aligned");
-    const int H = h->cfg.hidden;
-    hipLaunchKernelGGL(mt::moe_tail_out_proj_kernel, dim3((H + mt::OP_H - 1) / mt::OP_H, (rows + mt::MAX_R - 1) / mt::MAX_R),
-                       dim3(mt::OP_NT), 0, (hipStream_t)stream,
-                       (const uint16_t*)a->attn, (const uint16_t*)a->w_o, h->xbuf, rows, h->cfg.attn_dim, H);
-    HIPCHK(h, hipGetLastError());
-    fa = *a;
-    fa.x = h->xbuf;
-    a = &fa;
+    if (h->cfg.fold_norm) return fail(h, MOE_TAIL_EUNSUPPORTED, "the folded norm does not take attn (it reads x by chunks)");
   }
   if (rows <= mt::MAX_R) return run_launch(h, rows, a, stream);
   // More rows than one launch's MFMA columns: balanced row ranges, one
@@ -2136,6 +2214,7 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
       return q ? (void*)((const uint32_t*)q + (size_t)r0 * per_row) : nullptr;
     };
     b.x = off16(a->x, H);
+    b.attn = off16(a->attn, (size_t)h->cfg.attn_dim);
     b.residual = off16(a->residual, H);
     b.out = (uint16_t*)off16(a->out, H);
     b.res_out = (uint16_t*)off16(a->res_out, H);

@@ -133,9 +133,10 @@ typedef struct {
                                gate-sigmoid-mul-add on the shared expert); ignored when Is == 0 */
   /* the out_proj front ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation and
      Modifications: the fused launch starts with the attention output projection).  When attn is
-     given, x must be NULL: the library first computes x = bf16(attn . w_o^T) per row, the sum in
-     double and rounded once, into handle scratch (a launch of its own before the tail), and the
-     tail takes that x.  One rank's share: on one GPU its partial stands for the all-reduced sum. */
+     given, x must be NULL: the same launch computes x = bf16(attn . w_o^T) per row, each element
+     summed in double and rounded once (every workgroup its own slice of the hidden columns), and
+     the tail continues on that x.  One rank's share: on one GPU its partial stands for the
+     all-reduced sum. */
   const void* attn;         /* [rows, A] bf16 attention output rows (this rank's slice), or NULL */
   const void* w_o;          /* [H, A] bf16 out_proj columns of this rank, required with attn */
 } moe_tail_args;
