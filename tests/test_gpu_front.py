@@ -1,8 +1,10 @@
 """The out_proj front on the GPU: x = bf16(attn . w_o^T) for one rank's
 share ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation and
-Modifications), computed by the library before the tail, against the
+Modifications), computed in the same launch as the tail, against the
 oracle's out_proj and tail.  x is compared bit for bit (both sides sum in
 double and round once); the tail's outputs to the usual bars."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -65,3 +67,8 @@ def test_front_refusals():
     with pytest.raises(binding.MoeTailError) as ei:
         run(handle_for(cfg, attn_dim=128), cfg, dw, None, None, front=(da, None))
     assert ei.value.status == binding.EINVAL
+    # the folded norm reads x by K chunks: it takes no attention rows
+    folded = dataclasses.replace(cfg, fold_norm=1)
+    with pytest.raises(binding.MoeTailError) as ei:
+        run(handle_for(folded, attn_dim=128), folded, dw, None, None, front=(da, dwo))
+    assert ei.value.status == binding.EUNSUPPORTED
