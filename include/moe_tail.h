@@ -68,8 +68,10 @@ typedef enum { MOE_TAIL_MXFP4 = 0, MOE_TAIL_MXFP8 = 1 } moe_tail_weight_format;
 
 typedef struct {
   int32_t max_rows;     /* largest `rows` any run will pass: 1..32 (above 16, see moe_tail_run) */
-  int32_t hidden;       /* H: multiple of 128, 128..16384; moe_tail_create also refuses (EUNSUPPORTED) more than
-                           32 hidden rows per compute unit, i.e. H > 8192 on a 256-CU device */
+  int32_t hidden;       /* H: multiple of 128, 128..16384 (a routed gate/up load step covers 128 columns of a
+                           row: four 32-element scale blocks, one 16-byte load per lane; a norm slice is
+                           H/16 columns in 8-element vectors); moe_tail_create also refuses (EUNSUPPORTED)
+                           more than 32 hidden columns per compute unit, i.e. H > 8192 on a 256-CU device */
   int32_t num_experts;  /* E: 1..512 */
   int32_t top_k;        /* K: 1..min(E, 32) */
   int32_t inter;        /* I, per-rank expert intermediate: multiple of 32, 32..4096 */
