@@ -36,12 +36,10 @@
 //
 // Cross-workgroup exchange goes through handle-owned scratch.  Every
 // workgroup counts the calls it has started (its epoch).  On the router chain
-// and for both products' activations the data carry the epoch as a tag (xn
-// chunks, router partials, logits, the shared and routed a), so a reader
-// polls the data themselves, and a down product starts on an expert as soon
-// as that expert's gate/up units are done, with no barrier behind all of
-// them; elsewhere counters in two banks, selected by the epoch's parity,
-// release the readers, and no reset is needed between calls or graph replays.  Every wait has a deadline and a shared
+// the data carry the epoch as a tag (xn chunks, router partials, logits), so
+// a reader polls the data themselves; elsewhere counters in two banks,
+// selected by the epoch's parity, release the readers, and no reset is needed
+// between calls or graph replays.  Every wait has a deadline and a shared
 // abort word (K2 commit text, Motivation: each wait has a deadline, a failed
 // wait stops the launch everywhere; "Split the Kimi3 AttnRes mix across CTAs
 // for decode rows", design section: per-call tags in the exchanged words).
@@ -173,8 +171,8 @@ struct Params {
   uint64_t* gpart;  // [R][NQ] tagged fp32 partial dots of the shared gate, one per norm slice
   uint64_t* rstdt;  // [R] tagged fp32 rstd of each row (folded norm)
   uint64_t* xft;    // [R][H/2] tagged x pairs computed by the out_proj front, one slice per workgroup
-  uint64_t* ast;  // [R][Is/2] tagged shared a, two bf16 (i, i + 1) per word
-  uint64_t* art;  // [P][I/2] tagged routed a, the same way
+  uint16_t* a_s;
+  uint16_t* a_r;
 };
 
 // ------------------------------------------------------------------ helpers --
@@ -517,7 +515,6 @@ struct Shared {
   float w[MAX_P];
   int16_t ci[MAX_P];
   uint32_t rowmask[MAX_E];
-  uint32_t rbad[MAX_P / 32];  // routed a rows whose first poll found a word of an earlier call
   int16_t eslot[MAX_E];
   int16_t slot_expert[MAX_P];
   uint16_t slot_mask[MAX_P];
@@ -544,8 +541,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const rsrc_t rs_xt = make_rsrc(p.xnt, (uint32_t)(R * H * 4));
   const rsrc_t rs_lt = make_rsrc(p.lgt, (uint32_t)(R * p.Ep * 8));
   const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * 2048));
-  const rsrc_t rs_as = make_rsrc(p.ast, (uint32_t)(R * Is * 4));
-  const rsrc_t rs_ar = make_rsrc(p.art, (uint32_t)(P * I * 4));
+  const rsrc_t rs_as = make_rsrc(p.a_s, (uint32_t)(R * Is * 2));
+  const rsrc_t rs_ar = make_rsrc(p.a_r, (uint32_t)(P * I * 2));
   uint16_t* xl = (uint16_t*)dyn;  // [xrows][xs] staged activations; row xzero is zeros
   uint16_t* xc = (uint16_t*)dyn;  // [xrows][cs] this workgroup's K chunk of them (same space, earlier)
   const int xzero = p.xzero;
@@ -567,18 +564,16 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     cr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.res ? p.res : p.gamma, p.res ? (uint32_t)(R * H * 2) : 0u),
                                               (int)off, 0, 0);
   }
-  TL(30);
   // ---- call epoch: every workgroup counts the calls it has started, so all
   // agree on it without a shared ticket (one launch = one call per workgroup).
-  // Only this workgroup touches its count, and the calls on a device run one
-  // after another, so a device-scope load now and a store of the new value
-  // once it has returned do what a read-modify-write would, with a shorter
-  // round trip; nothing waits for the load until the epoch is first needed.
+  // The count is a read-modify-write atomic, like every other control word
+  // that crosses workgroups or calls; nothing waits for its return until the
+  // epoch is first needed.
   uint32_t epv = 0;
   if (tid == 0) {
-    int z;  // an index the compiler cannot see is uniform: the load is issued as written, with no wait after it
+    int z;  // an index the compiler cannot see is uniform: the atomic is issued as written, with no wait after it
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-    epv = __hip_atomic_load(&p.ctl->cta_ep[cta][z], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    epv = __hip_atomic_fetch_add(&p.ctl->cta_ep[cta][z], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid < E) S.rowmask[tid] = 0u;
   if (tid == 0) S.flags[5] = 0u;  // set by a top-k wave whose logits poll gave up
@@ -804,12 +799,10 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         ss = fma(h1, h1, ss);
       }
     }
-    TL(25);
     ss = wave_sum_f64(ss);
     if (lane == 0) S.tmpd[wave] = ss;
-    if (tid == 0) S.ep = epv + 1u;  // the epoch load went out before the row loads
+    if (tid == 0) S.ep = epv + 1u;  // the epoch atomic went out before the row loads
     __syncthreads();
-    TL(26);
     const uint32_t epn = S.ep;
     double tot = 0.0;
     for (int w = 0; w < NW; ++w) tot += S.tmpd[w];
@@ -833,7 +826,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       if (p.res_out) *(u32x4*)(p.res_out + (size_t)row * H + i) = hv;
       nvs = nv;
     }
-    TL(27);
     if (FEAT && p.fold && q == 0 && tid == 0) st_tag(p.rstdt + row, __float_as_uint((float)rstd), epn);
     if (FEAT && p.sgate) {  // this slice's share of the gate's dot product: lanes, waves in order
       float gd = 0.f;
@@ -881,12 +873,10 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   }
   if (tid == 0) {
     uint32_t e1 = epv;
-    asm volatile("" : "+v"(e1));  // keeps the wait for the load's return here
+    asm volatile("" : "+v"(e1));  // keeps the wait for the atomic's return here
     S.ep = e1 + 1u;
-    __hip_atomic_store(&p.ctl->cta_ep[cta][0], e1 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  TL(29);
   const uint32_t ep = S.ep;
   Bank* bk = &p.ctl->bank[ep & 1];
   if (cta == 0) {  // the next call's counters, with write-through (SC1) stores
@@ -896,7 +886,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   }
   if (is_norm) {
     publish(&bk->normc[cta % NQ][0], 1);
-    TL(28);
     w1.prime(p1_next);
   }
   TL(1);
@@ -1017,37 +1006,31 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     __syncthreads();
     const int ns = S.nls;
-    // thread (block, column col, pair pp): a of the block's rows 2 pp and 2 pp + 1,
-    // stored as one tagged word (the down phase polls the words themselves)
-    for (int idx = tid; idx < ns * 4 * R; idx += NT) {
-      const int k = idx / (4 * R), rc = idx - k * 4 * R, col = rc >> 2, pp = rc & 3;
+    for (int idx = tid; idx < ns * 8 * R; idx += NT) {
+      const int k = idx / (8 * R), rc = idx - k * 8 * R, col = rc >> 3, row = rc & 7;
       const int sb = S.lsb[k], u = n_rb + sb;
-      uint32_t ab[2];
+      float tg[NQ], tu[NQ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 2 * pp + j;
-        float tg[NQ], tu[NQ];
-#pragma unroll
-        for (int s = 0; s < NQ; ++s)
-          if (s < S1) {
-            tg[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
-            tu[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row + 8));
-          }
-        float gs = 0.f, us = 0.f;
-#pragma unroll
-        for (int s = 0; s < NQ; ++s)
-          if (s < S1) {
-            gs += tg[s];
-            us += tu[s];
-          }
-        if (FEAT && p.fold) {
-          gs *= S.rstd[col];
-          us *= S.rstd[col];
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1) {
+          tg[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
+          tu[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row + 8));
         }
-        ab[j] = f2bf(gs / (1.f + __expf(-gs)) * us);
+      float gs = 0.f, us = 0.f;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s)
+        if (s < S1) {
+          gs += tg[s];
+          us += tu[s];
+        }
+      if (FEAT && p.fold) {
+        gs *= S.rstd[col];
+        us *= S.rstd[col];
       }
-      st_tag(p.ast + (size_t)col * (Is / 2) + sb * 4 + pp, ab[0] | (ab[1] << 16), ep);
+      const float a = gs / (1.f + __expf(-gs)) * us;
+      stc2(rs_as, (uint32_t)(col * Is + sb * 8 + row) * 2u, f2bf(a));
     }
+    if (ns) publish(&bk->shared[0], (uint32_t)ns);
   }
   TL(4);
 
@@ -1313,17 +1296,16 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       const int m = __popc((uint32_t)S.slot_mask[d]);
       S.red[rb][wave][lane] = acc;
       __syncthreads();
-      if (tid < 64) {  // thread (pair pp, column col): a of intermediate indices 2 pp and 2 pp + 1
-        const int col = tid & 15, pp = tid >> 4, l = 16 * (pp >> 1) + col, q0 = 2 * (pp & 1);
-        float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+      if (tid < 128) {
+        const int l = tid >> 2, qq = tid & 3;
+        float gs = 0.f, us = 0.f;
         for (int w = 0; w < NW; ++w) {
-          g0 += S.red[rb][w][l][q0];
-          g1 += S.red[rb][w][l][q0 + 1];
-          u0 += S.red[rb][w][l + 32][q0];
-          u1 += S.red[rb][w][l + 32][q0 + 1];
+          gs += S.red[rb][w][l][qq];
+          us += S.red[rb][w][l + 32][qq];
         }
-        const float a0 = g0 / (1.f + __expf(-g0)) * u0, a1 = g1 / (1.f + __expf(-g1)) * u1;
-        if (col < m) st_tag(p.art + (size_t)(S.slot_off[d] + col) * (I / 2) + bb * 4 + pp, f2bf(a0) | (f2bf(a1) << 16), ep);
+        const int ii = 4 * (l >> 4) + qq, col = l & 15;
+        const float a = gs / (1.f + __expf(-gs)) * us;
+        if (col < m) stc2(rs_ar, (uint32_t)((S.slot_off[d] + col) * I + bb * 8 + ii) * 2u, f2bf(a));
       }
       rb ^= 1;
     };
@@ -1454,6 +1436,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         }
       });
     }
+    if (nu2) publish(&bk->routed[cta % NRC][0], (uint32_t)nu2);
   }
   TL(8);
 
@@ -1505,113 +1488,71 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     return f;
   };
-  if (hn == 0) return;  // no output rows here
-  // The down weights go out first (routed, then shared): nothing below needs
-  // them until the activations are in LDS.
+  // the shared gate of every row: the norm slices' partial dots, long written
+  // by now, summed in slice order (before the down weights' loads go out)
+  if (FEAT && p.sgate && Is > 0 && hn > 0) {
+    if (!poll_all([&]() {
+          bool ok = true;
+          if (tid < R * NQ) {
+            const uint64_t w = ld_tag(p.gpart + tid);
+            ok = tag_ok(w, ep);
+            S.gsum[tid] = __uint_as_float((uint32_t)w);
+          }
+          return ok;
+        }, 2, 1, false))
+      return;
+    if (tid < R) {
+      float t = 0.f;
+      for (int q = 0; q < NQ; ++q) t += S.gsum[tid * NQ + q];
+      S.sgw[tid] = 1.f / (1.f + __expf(-t));
+    }
+    __syncthreads();
+  }
   Window<2, FragD<F8>> w3;
   w3.prime(p3_next);
-  const int Cs = Is / 32, CP = (Cs + NW - 1) / NW, c0 = wave * CP;  // shared down: waves split the Is/32 chunks
-  const rsrc_t rq_sd = make_rsrc(p.ws2 + (size_t)h0 * Is, (uint32_t)(hn * Is * 2));
-  int cs = c0;
-  auto sd_next = [&]() {
-    FragSD f;
-#pragma unroll
-    for (int bl = 0; bl < MAX_BLK; ++bl) {
-      const int hh = 16 * bl + i16;
-      f.a[bl] = ld16<CP_W>(rq_sd, (cs < c0 + CP && cs < Cs && bl < nblk && hh < hn) ? (uint32_t)(hh * Is + cs * 32 + g * 8) * 2u : OOB);
-    }
-    ++cs;
-    return f;
-  };
-  Window<4, FragSD> ws;
-  ws.prime(sd_next);
   TL(9);
-  // ---- the activations of both down products: tagged words (two bf16 each).
-  // The shared a [R][Is/2] was stored in the router/shared phase; the routed
-  // a [P][I/2] is stored by each slot's gate/up units as they finish, with
-  // no barrier behind all of them.  One pass of the whole workgroup copies
-  // every row into LDS and marks what still held a word of an earlier call:
-  // the shared a is then polled again by the whole workgroup, and the rows of
-  // a routed slot by the one wave that takes that slot, when it reaches it.
-  const int IW = I / 2;  // words per pick row
-  {
-    if (tid < P) {  // pick -> its product row: the slot's users in row order
-      const int d = S.eslot[S.ids[tid]], r = tid / K;
-      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
-    }
-    if (tid < MAX_P / 32) S.rbad[tid] = 0u;
-    if (tid < 8) S.flags[tid] = 0u;
-    __syncthreads();
-    const int nqr = P * IW / 2, nq = nqr + R * Is / 4;  // 16-byte loads: routed rows, then shared rows
-    constexpr int B = 12;
-    for (int base = 0; base < nq; base += NT * B) {
-      u32x4 v[B];
+  if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
+    return;
+  if (hn == 0) return;
+  {  // stage the shared a [R][Is] into LDS, plus its zero row
+    const int ns8 = R * Is / 8;
+    for (int base = 0; base < ns8; base += NT * 4) {
+      u32x4 v[4];
 #pragma unroll
-      for (int k = 0; k < B; ++k) {
-        const int q = base + k * NT + tid;
-        v[k] = q < nqr ? ld_tag2(rs_ar, (uint32_t)(2 * q)) : ld_tag2(rs_as, q < nq ? (uint32_t)(2 * (q - nqr)) : OOB / 8u);
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        v[k] = ld16<CP_SC1>(rs_as, e8 < ns8 ? (uint32_t)e8 * 16u : OOB);
       }
 #pragma unroll
-      for (int k = 0; k < B; ++k) {
-        const int q = base + k * NT + tid;
-        const bool ok = v[k][1] == ep && v[k][3] == ep;
-        if (q < nqr) {
-          const int row = (2 * q) / IW, c = 2 * q - row * IW;
-          *(uint2*)(al + row * p.as + 2 * c) = make_uint2(v[k][0], v[k][2]);
-          if (!ok) atomicOr(&S.rbad[row >> 5], 1u << (row & 31));
-        } else if (q < nq) {
-          const int w = 2 * (q - nqr), row = w / (Is / 2), c = w - row * (Is / 2);
-          *(uint2*)(asl + row * p.ss + 2 * c) = make_uint2(v[k][0], v[k][2]);
-          if (!ok) S.flags[3] = 1u;
-        }
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        if (e8 < ns8) *(u32x4*)(asl + ((e8 * 8) / Is) * p.ss + (e8 * 8) % Is) = v[k];
       }
     }
-    if (FEAT && p.sgate && Is > 0 && tid < R * NQ) {  // the shared gate: the norm slices' partial dots
-      const uint64_t w = ld_tag(p.gpart + tid);
-      S.gsum[tid] = __uint_as_float((uint32_t)w);
-      if (!tag_ok(w, ep)) S.flags[2] = 1u;
-    }
-    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
     for (int c = tid * 8; c < p.ss; c += NT * 8) *(u32x4*)(asl + szero * p.ss + c) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
-    if (S.flags[3]) {  // the shared a again, all of it, until every word is this call's
-      const int nqs = R * Is / 4;
-      if (!poll_all([&]() {
-            bool ok = true;
-            for (int q = tid; q < nqs; q += NT) {
-              const u32x4 v = ld_tag2(rs_as, (uint32_t)(2 * q));
-              ok = ok && v[1] == ep && v[3] == ep;
-              const int w = 2 * q, row = w / (Is / 2), c = w - row * (Is / 2);
-              *(uint2*)(asl + row * p.ss + 2 * c) = make_uint2(v[0], v[2]);
-            }
-            return ok;
-          }, 2, (uint32_t)D, false))
-        return;
-    }
-    if (FEAT && p.sgate && Is > 0) {
-      if (S.flags[2] && !poll_all([&]() {
-            if (tid >= R * NQ) return true;
-            const uint64_t w = ld_tag(p.gpart + tid);
-            S.gsum[tid] = __uint_as_float((uint32_t)w);
-            return tag_ok(w, ep);
-          }, 2, 1, false))
-        return;
-      if (tid < R) {  // sigmoid of the slices' sum, in slice order
-        float t = 0.f;
-        for (int q = 0; q < NQ; ++q) t += S.gsum[tid * NQ + q];
-        S.sgw[tid] = 1.f / (1.f + __expf(-t));
-      }
-      __syncthreads();
-    }
   }
-  TL(10);
-  // shared down
+  // shared down: waves split the Is/32 chunks
   if (Is > 0) {
+    const int Cs = Is / 32, CP = (Cs + NW - 1) / NW, c0 = wave * CP;
+    const rsrc_t rq = make_rsrc(p.ws2 + (size_t)h0 * Is, (uint32_t)(hn * Is * 2));
     f32x4 acc[MAX_BLK];
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    int cu = c0;
+    Window<4, FragSD> ws;
+    int cs = c0, cu = c0;
+    auto sd_next = [&]() {
+      FragSD f;
+#pragma unroll
+      for (int bl = 0; bl < MAX_BLK; ++bl) {
+        const int hh = 16 * bl + i16;
+        f.a[bl] = ld16<CP_W>(rq, (cs < c0 + CP && cs < Cs && bl < nblk && hh < hn) ? (uint32_t)(hh * Is + cs * 32 + g * 8) * 2u : OOB);
+      }
+      ++cs;
+      return f;
+    };
     const int srow = (i16 < R ? i16 : szero) * p.ss + g * 8;
+    ws.prime(sd_next);
     ws.run(CP, sd_next, [&](const FragSD& f) {
       const u32x4 b = lds16(asl + (cu < Cs ? srow + cu * 32 : szero * p.ss));
 #pragma unroll
@@ -1630,26 +1571,33 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       }
     }
   }
-  // rows [ci0, ci0 + m) of one slot, polled by this wave until every word is
-  // this call's; false when the call is aborted
-  auto poll_slot = [&](int ci0, int m) -> bool {
-    const unsigned long long t0 = wall_clock64();
-    const int nq = m * IW / 2;
-    for (;;) {
-      bool ok = true;
-      for (int q = lane; q < nq; q += 64) {
-        const u32x4 v = ld_tag2(rs_ar, (uint32_t)(ci0 * IW + 2 * q));
-        ok = ok && v[1] == ep && v[3] == ep;
-        const int row = (2 * q) / IW, c = 2 * q - row * IW;
-        *(uint2*)(al + (ci0 + row) * p.as + 2 * c) = make_uint2(v[0], v[2]);
-      }
-      if (__ballot(!ok) == 0) return true;
-      if (give_up(p, bk, t0, 3, 0u, 1u, ep, (uint32_t)D)) return false;
-      __builtin_amdgcn_s_sleep(1);
+  // routed down: it needs every slot's a, so it waits for all gate/up units
+  if (!wait_cnt<true>(p, bk, &bk->routed[0][0], 16, NRC, (uint32_t)(D * (I / 8)), false, &S.flags[4], 3, ep, (uint32_t)D))
+    return;
+  TL(10);
+  {  // stage the routed a [P][I] into LDS, plus its zero row
+    if (tid < P) {  // pick -> its product row: the slot's users in row order
+      const int d = S.eslot[S.ids[tid]], r = tid / K;
+      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
     }
-  };
+    const int nr8 = P * I / 8;
+    for (int base = 0; base < nr8; base += NT * 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        v[k] = ld16<CP_SC1>(rs_ar, e8 < nr8 ? (uint32_t)e8 * 16u : OOB);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e8 = base + k * NT + tid;
+        if (e8 < nr8) *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+      }
+    }
+    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
-  bool aborted = false;
   {
     f32x4 acc[MAX_BLK];
 #pragma unroll
@@ -1658,11 +1606,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     w3.run(nsl * NP3, p3_next, [&](const FragD<F8>& f) {
       const int d = wave + NW * ju;
       const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
-      if (qu == 0 && !aborted) {  // first frag of the slot: are all its rows this call's?
-        bool bad = false;
-        for (int r = ci0; r < ci0 + m; ++r) bad = bad || ((S.rbad[r >> 5] >> (r & 31)) & 1u);
-        if (bad && !poll_slot(ci0, m)) aborted = true;
-      }
       const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -1705,9 +1648,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     });
   }
   TL(11);
-  if (aborted && lane == 0) S.flags[4] = 1u;
   __syncthreads();
-  if (S.flags[4]) return;  // a wave's poll of the routed a gave up: the call is aborted
   // combine in a fixed order: picks in (row, k) order, then the shared part
   if (tid < R * hn) {
     const int r = tid / hn, hh = tid % hn, h = h0 + hh;
@@ -1831,8 +1772,8 @@ struct moe_tail {
   uint64_t* gpart;
   uint64_t* rstdt;
   size_t scratch_bytes;
-  uint64_t* ast;
-  uint64_t* art;
+  uint16_t* a_s;
+  uint16_t* a_r;
   int S1, TC, n_rb, n_sb, Ep;
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
   int sticky;       // 1: an unread timeout makes later calls give up at once (handles); 0: each call starts clean
@@ -1982,8 +1923,8 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
   L->o_gp = L->o_pt + al((size_t)n_it * 2048);
   L->o_rs = L->o_gp + al(R * mt::NQ * 8);
   L->o_as = L->o_rs + al(R * 8);
-  L->o_ar = L->o_as + al(R * (Is ? Is : 2) * 4);
-  L->o_xf = L->o_ar + al(R * K * I * 4);
+  L->o_ar = L->o_as + al(R * (Is ? Is : 1) * 2);
+  L->o_xf = L->o_ar + al(R * K * I * 2);
   L->total = L->o_xf + (cfg->attn_dim > 0 ? al(R * H * 4) : 0);
   snprintf(h->err, sizeof(h->err), "no error");
   return MOE_TAIL_OK;
@@ -2001,8 +1942,8 @@ static void place_scratch(moe_tail_t* h, const ScratchLayout& L, void* base_) {
   h->part1 = (uint64_t*)(base + L.o_pt);
   h->gpart = (uint64_t*)(base + L.o_gp);
   h->rstdt = (uint64_t*)(base + L.o_rs);
-  h->ast = (uint64_t*)(base + L.o_as);
-  h->art = (uint64_t*)(base + L.o_ar);
+  h->a_s = (uint16_t*)(base + L.o_as);
+  h->a_r = (uint16_t*)(base + L.o_ar);
   h->xft = h->cfg.attn_dim > 0 ? (uint64_t*)(base + L.o_xf) : nullptr;
 }
 
@@ -2173,8 +2114,8 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.part1 = h->part1;
   p.gpart = h->gpart;
   p.rstdt = h->rstdt;
-  p.ast = h->ast;
-  p.art = h->art;
+  p.a_s = h->a_s;
+  p.a_r = h->a_r;
 
   // A plain launch, eager or captured alike: create() has checked that one
   // workgroup fits on every compute unit, so all G are resident together on
