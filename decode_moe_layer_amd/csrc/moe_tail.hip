@@ -133,6 +133,7 @@ struct Params {
   int off_as, off_outp, off_shp;  // byte offsets in dynamic LDS (down phase)
   int xzero, azero, szero;        // indices of the all-zero LDS rows (inactive MFMA columns)
   int n_rb, n_sb;                 // router blocks (16 experts), shared blocks (8 gate + 8 up rows)
+  int nn1;                        // leading workgroups that take no router/shared items (the norm's, at few rows)
   int S1, TC;                     // K chunks per block, 32-column groups per chunk
   int Ep;                         // logits row stride (E rounded up to 8)
   double eps;
@@ -548,6 +549,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int xzero = p.xzero;
 
   TL(0);
+  {  // Every 64-byte line of the kernel arguments at once: the first use of
+     // each line would otherwise be a miss of its own, one after another.
+    static_assert(sizeof(Params) <= 448, "the lines touched below cover the arguments");
+    const char* kp = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const uint32_t k0 = *(const uint32_t*)(kp + 64), k1 = *(const uint32_t*)(kp + 128), k2 = *(const uint32_t*)(kp + 192);
+    const uint32_t k3 = *(const uint32_t*)(kp + 256), k4 = *(const uint32_t*)(kp + 320), k5 = *(const uint32_t*)(kp + 384);
+    asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5));
+  }
   // This workgroup's output rows [h0, h0 + hn) of the combine (R hn <= NT: one
   // element per thread; an even width HR).  Their x and residual are loaded
   // now, so that the combine at the end does not wait for memory.
@@ -579,19 +588,25 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   if (tid == 0) S.flags[5] = 0u;  // set by a top-k wave whose logits poll gave up
   const bool stall = (p.debug_flags & MOE_TAIL_DEBUG_STALL) && cta == p.debug_block;
 
-  // ---- router/shared source.  Item i = cta, cta + G, ... is K chunk i % S1 of
-  // block i / S1 (router blocks of 16 experts, then shared blocks of 8 gate +
-  // 8 up rows); S1 divides G, so all of this workgroup's items share chunk s1.
+  // ---- router/shared source.  Item i = wi, wi + W1, ... (below) is K chunk
+  // i % S1 of block i / S1 (router blocks of 16 experts, then shared blocks of
+  // 8 gate + 8 up rows); S1 divides W1, so all of a workgroup's items share
+  // chunk s1.
   // Wave w streams the chunk's 32-column groups [t01, t1e).
   const int s1 = cta % S1;
   const int TP1 = (TC + NW - 1) / NW, t01 = wave * TP1, t1e = min(TC, t01 + TP1);
-  const int nu1 = cta < n_it ? (n_it - 1 - cta) / G + 1 : 0;
+  // With few rows the first nn1 workgroups (those that run the norm) take no
+  // items: theirs would start last, behind the norm, and every router block
+  // waits for its slowest chunk.  The others share the items round-robin (W1
+  // of them; nn1 is a multiple of S1, so workgroup cta still takes chunk s1).
+  const int W1 = G - p.nn1, wi = cta - p.nn1;
+  const int nu1 = wi >= 0 && wi < n_it ? (n_it - 1 - wi) / W1 + 1 : 0;
   Window<D_BF, FragA> w1;
   int k1 = 0, t1 = t01;
   uint32_t roff1 = OOB;
   rsrc_t rs1 = make_rsrc(p.rw, (uint32_t)((size_t)E * H * 2));
   auto p1_unit = [&]() {  // decode item k1
-    const int u = (cta + k1 * G) / S1;
+    const int u = (wi + k1 * W1) / S1;
     int row;
     if (u < n_rb) {
       row = u * 16 + i16 < E ? u * 16 + i16 : -1;
@@ -938,7 +953,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       acc = mfma(as_bf16x8(f.a), as_bf16x8(b), acc);
       if (++tt == TP1) {  // item done: reduce the 8 waves' partials in wave order, store the chunk's partial
         tt = 0;
-        const int it = cta + kk * G;
+        const int it = wi + kk * W1;
         ++kk;
         S.red[rb][wave][lane] = acc;
         acc = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -967,7 +982,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid < nu1) {
-    const int u = (cta + tid * G) / S1;
+    const int u = (wi + tid * W1) / S1;
     const uint32_t old = __hip_atomic_fetch_add(&bk->unitc[u][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.last[tid] = old == (uint32_t)(S1 - 1);
   }
@@ -975,7 +990,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   {
     int nr = 0;
     for (int k = 0; k < nu1; ++k) {  // router blocks: logits = sum of the chunks in chunk order
-      const int u = (cta + k * G) / S1;
+      const int u = (wi + k * W1) / S1;
       if (!S.last[k] || u >= n_rb || RS) continue;
       if (tid < 16 * R) {
         const int col = tid >> 4, row = tid & 15;
@@ -999,7 +1014,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     if (tid == 0) {
       int ns = 0;
       for (int k = 0; k < nu1; ++k) {
-        const int u = (cta + k * G) / S1;
+        const int u = (wi + k * W1) / S1;
         if (S.last[k] && u >= n_rb) S.lsb[ns++] = (int16_t)(u - n_rb);
       }
       S.nls = ns;
@@ -2063,6 +2078,15 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.cs = h->plan.cs;
   p.n_rb = h->n_rb;
   p.n_sb = h->n_sb;
+  {  // the norm's workgroups take no router/shared items when they are few
+     // (up to 2 rows: measured faster at 1 and 2 rows; at 4 rows it depends
+     // on the shape, slower at c1's and faster at c3's, so it stays off)
+    const int nn = rows * mt::NQ;
+    p.nn1 = nn <= 2 * mt::NQ && nn % h->S1 == 0 && h->G - nn >= h->S1 &&
+                    ((h->n_rb + h->n_sb) * h->S1 + (h->G - nn) - 1) / (h->G - nn) <= mt::MAX_ITEMS1
+                ? nn
+                : 0;
+  }
   p.S1 = h->S1;
   p.TC = h->TC;
   p.Ep = h->Ep;
