@@ -1299,7 +1299,13 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   {
     const int UB = I / 8, n_p2 = D * UB;
     const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW, t02 = wave * TP2;
-    const int u0 = cta;
+    // Units go round-robin from workgroup off2 on: the workgroups before it
+    // reach this phase last (the norm's, or those with one more router/shared
+    // item), so the units left over after whole rounds go to early ones.  off2
+    // is a multiple of 8, which keeps each unit on the same XCD.
+    int off2 = p.nn1 ? p.nn1 + n_it % (G - p.nn1) : max(R * NQ, n_it % G);
+    off2 = (off2 & ~7) % G;
+    const int u0 = cta >= off2 ? cta - off2 : cta + G - off2;
     const int nu2 = u0 < n_p2 ? (n_p2 - 1 - u0) / G + 1 : 0;
     // codes per expert: MXFP4 packs two per byte, MXFP8 one
     const int RB13 = F8 ? H : H / 2;
