@@ -1111,6 +1111,26 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       return;
   }
   TL(5);
+  // The shared expert's down weights for this workgroup's hidden rows do not
+  // depend on the routing: their first loads go out here, while the memory
+  // system is quiet, and stay in registers until the down phase uses them.
+  const int nblk = (hn + 15) / 16;
+  const int Cs = Is / 32, CPs = (Cs + NW - 1) / NW, c0s = wave * CPs;
+  const rsrc_t rqs = make_rsrc(p.ws2 + (size_t)h0 * Is, (uint32_t)(hn * Is * 2));
+  int cse = c0s;
+  auto sd_next = [&]() {  // every load is issued (out of range where not needed): the waits stay counted
+    FragSD f;
+#pragma unroll
+    for (int bl = 0; bl < MAX_BLK; ++bl) {
+      const int hh = 16 * bl + i16;
+      const bool v = cse < c0s + CPs && cse < Cs && bl < nblk && hh < hn;
+      f.a[bl] = ld16<CP_W>(rqs, v ? (uint32_t)(hh * Is + cse * 32 + g * 8) * 2u : OOB);
+    }
+    ++cse;
+    return f;
+  };
+  Window<2, FragSD> ws;
+  ws.prime(sd_next);
   for (int r = wave; r < R; r += NW) {
     const int e0 = 8 * lane;
     float lg[8];
@@ -1462,7 +1482,6 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   TL(8);
 
   // ---- P3: down projections for this workgroup's hidden rows, then combine
-  const int nblk = (hn + 15) / 16;
   const int CI = I / 32, TI = (CI + 3) / 4;
   const int nsl = D > wave ? (D - wave + NW - 1) / NW : 0;
   const int RB2 = F8 ? I : I / 2;  // down code bytes per hidden row
@@ -1553,28 +1572,14 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     for (int c = tid * 8; c < p.ss; c += NT * 8) *(u32x4*)(asl + szero * p.ss + c) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
   }
-  // shared down: waves split the Is/32 chunks
+  // shared down: waves split the Is/32 chunks (their first weight loads went out before top-k)
   if (Is > 0) {
-    const int Cs = Is / 32, CP = (Cs + NW - 1) / NW, c0 = wave * CP;
-    const rsrc_t rq = make_rsrc(p.ws2 + (size_t)h0 * Is, (uint32_t)(hn * Is * 2));
     f32x4 acc[MAX_BLK];
 #pragma unroll
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    Window<4, FragSD> ws;
-    int cs = c0, cu = c0;
-    auto sd_next = [&]() {
-      FragSD f;
-#pragma unroll
-      for (int bl = 0; bl < MAX_BLK; ++bl) {
-        const int hh = 16 * bl + i16;
-        f.a[bl] = ld16<CP_W>(rq, (cs < c0 + CP && cs < Cs && bl < nblk && hh < hn) ? (uint32_t)(hh * Is + cs * 32 + g * 8) * 2u : OOB);
-      }
-      ++cs;
-      return f;
-    };
+    int cu = c0s;
     const int srow = (i16 < R ? i16 : szero) * p.ss + g * 8;
-    ws.prime(sd_next);
-    ws.run(CP, sd_next, [&](const FragSD& f) {
+    ws.run(CPs, sd_next, [&](const FragSD& f) {
       const u32x4 b = lds16(asl + (cu < Cs ? srow + cu * 32 : szero * p.ss));
 #pragma unroll
       for (int bl = 0; bl < MAX_BLK; ++bl)
