@@ -1129,8 +1129,11 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     ++cse;
     return f;
   };
+  // (With the optional steps, whose kernels hold more registers, only at 1-2
+  // rows; at more rows they prime it in the down phase, measured faster there.)
+  const bool wse = !FEAT || R <= 2;
   Window<2, FragSD> ws;
-  ws.prime(sd_next);
+  if (wse) ws.prime(sd_next);
   for (int r = wave; r < R; r += NW) {
     const int e0 = 8 * lane;
     float lg[8];
@@ -1579,6 +1582,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
     int cu = c0s;
     const int srow = (i16 < R ? i16 : szero) * p.ss + g * 8;
+    if (!wse) ws.prime(sd_next);
     ws.run(CPs, sd_next, [&](const FragSD& f) {
       const u32x4 b = lds16(asl + (cu < Cs ? srow + cu * 32 : szero * p.ss));
 #pragma unroll
