@@ -338,21 +338,25 @@ __device__ __forceinline__ int nth_bit(uint32_t m, int n) {
 // `use` consumes items in order, D items behind the loads.
 template <int D, class Frag>
 struct Window {
-  Frag buf[D];
+  Frag buf[D + 1];  // D in flight and the one in use
   template <class NextF>
   __device__ __forceinline__ void prime(NextF next) {
 #pragma unroll
     for (int j = 0; j < D; ++j) buf[j] = next();
   }
+  // Step j of each pass of D + 1 steps: the free slot (j + D) mod (D + 1)
+  // takes the next item's loads, then slot j is used.  A pass of D + 1 steps
+  // ends with every slot back in its own registers.  With passes of D steps
+  // the compiler copied the in-flight slots at the loop's back-edge, and a
+  // copy waits for its loads: the window emptied on every pass.
   template <class NextF, class UseF>
   __device__ __forceinline__ void run(int n, NextF next, UseF use) {
-    for (int base = 0; base < n; base += D) {
+    for (int base = 0; base < n; base += D + 1) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
+      for (int j = 0; j <= D; ++j) {
         if (base + j < n) {
-          Frag cur = buf[j];
-          buf[j] = next();
-          use(cur);
+          buf[(j + D) % (D + 1)] = next();
+          use(buf[j]);
         }
       }
     }
@@ -1389,7 +1393,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         }
         return f;
       };
-      Window<2, FragU> w2;
+      Window<1, FragU> w2;
       w2.prime(p2_next);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       int kk = 0, qc = 0;
@@ -1551,7 +1555,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     __syncthreads();
   }
-  Window<2, FragD<F8>> w3;
+  Window<1, FragD<F8>> w3;
   w3.prime(p3_next);
   TL(9);
   if (Is > 0 && !wait_cnt<false>(p, bk, &bk->shared[0], 16, 1, (uint32_t)n_sb, false, &S.flags[3], 2, ep, (uint32_t)D))
