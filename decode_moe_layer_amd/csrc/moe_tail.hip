@@ -74,18 +74,19 @@ namespace mt {
 constexpr int NT = 512;      // threads per workgroup
 constexpr int NW = NT / 64;  // waves per workgroup
 constexpr int NQ = 16;       // norm slices per row
-constexpr int MAX_R = 16;          // rows per launch (MFMA columns)
-constexpr int MAX_ROWS_CALL = 32;  // rows per call: more than MAX_R run as balanced launches
+constexpr int MAX_R = 16;          // rows per narrow launch (one tile of MFMA columns)
+constexpr int MAX_RW = 32;         // rows per wide launch (two tiles of MFMA columns)
+constexpr int MAX_ROWS_CALL = 32;  // rows per call
 constexpr int MAX_E = 512;
 constexpr int MAX_K = 32;
-constexpr int MAX_P = MAX_R * MAX_K;  // picks per call
+constexpr int MAX_P = MAX_R * MAX_K;  // picks per launch (a wide launch needs rows x top_k <= MAX_P)
 constexpr int MAX_BLK = 2;            // 16-row down blocks per workgroup
 constexpr int D_BF = 12;              // bf16 weight loads in flight per wave
 constexpr int D_FP4_G = 4;            // MXFP4 items in flight per wave when activations come from global memory
 constexpr int XPAD = 8;               // bf16 padding per LDS activation row
 constexpr int FRONT_AC = 1024;                       // out_proj front: attention columns per K chunk
 constexpr int FRONT_WV = FRONT_AC / 8 / 16;          // its weight vectors per thread and chunk
-constexpr int FRONT_AV = MAX_R * FRONT_AC / 8 / NT;  // its attention vectors per thread and chunk (staged in LDS)
+constexpr int FRONT_AV = MAX_R * FRONT_AC / 8 / NT;  // its attention vectors per thread and chunk (staged in LDS; narrow launches only)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -505,14 +506,17 @@ struct FragSD {
   u32x4 a[MAX_BLK];
 };
 
-struct Shared {
+template <bool WIDE>
+struct SharedT {
+  static constexpr int RW = WIDE ? MAX_RW : MAX_R;
+  typedef typename std::conditional<WIDE, uint32_t, uint16_t>::type mask_t;  // a slot's users (one bit per row)
   uint32_t flags[8];
   uint32_t ep;
   double tmpd[NW];
   float tmpg[NW];             // shared gate: each wave's partial dot of a norm slice
-  float rstd[MAX_R];          // folded norm: each row's rstd
-  float gsum[MAX_R * NQ];     // shared gate: the slices' partial dots, per row
-  float sgw[MAX_R];           // shared gate: sigmoid(wg . xn) per row
+  float rstd[RW];             // folded norm: each row's rstd
+  float gsum[RW * NQ];        // shared gate: the slices' partial dots, per row
+  float sgw[RW];              // shared gate: sigmoid(wg . xn) per row
   int wcnt[NW];
   int ucnt[NW];
   int last[MAX_ITEMS1];
@@ -522,19 +526,26 @@ struct Shared {
   uint32_t rowmask[MAX_E];
   int16_t eslot[MAX_E];
   int16_t slot_expert[MAX_P];
-  uint16_t slot_mask[MAX_P];
+  mask_t slot_mask[MAX_P];
   int16_t slot_off[MAX_P + 1];
   int nslot;
   int nls;
   int16_t lsb[MAX_ITEMS1];  // shared blocks this workgroup finishes
   f32x4 red[2][NW][64];
 };
-constexpr int RED_FLOATS = 2 * NW * 64 * 4;  // floats in Shared::red
+constexpr int RED_FLOATS = 2 * NW * 64 * 4;  // floats in SharedT::red
 
 // ------------------------------------------------------------------ kernel --
 
-template <bool XL, bool RS, bool FEAT, bool F8>
-__device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
+// WIDE: up to MAX_RW rows in one launch.  Where rows are MFMA columns (the
+// router/shared K chunks, the shared down) a weight load feeds two 16-column
+// tiles; an expert picked by more than 16 rows takes one slot per 16 of them
+// (gate/up and down units stay one tile wide); the down phase stages the
+// routed a in groups of slots that fit in LDS.
+template <bool XL, bool RS, bool FEAT, bool F8, bool WIDE>
+__device__ __forceinline__ void tail(const Params& p, SharedT<WIDE>& S, char* dyn) {
+  static_assert(!WIDE || (!XL && !RS), "a wide launch reads xn from global scratch and sums router partials once");
+  constexpr int PC = WIDE ? 32 : 16;  // columns per router/shared K-chunk partial tile
   const int tid = threadIdx.x, lane = tid & 63, cta = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int R = p.R, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, G = p.G;
@@ -545,7 +556,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const rsrc_t rs_xn = make_rsrc(p.xn, (uint32_t)(R * H * 2));
   const rsrc_t rs_xt = make_rsrc(p.xnt, (uint32_t)(R * H * 4));
   const rsrc_t rs_lt = make_rsrc(p.lgt, (uint32_t)(R * p.Ep * 8));
-  const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * 2048));
+  const rsrc_t rs_pt = make_rsrc(p.part1, (uint32_t)(n_it * PC * 128));
   const rsrc_t rs_as = make_rsrc(p.a_s, (uint32_t)(R * Is * 2));
   const rsrc_t rs_ar = make_rsrc(p.a_r, (uint32_t)(P * I * 2));
   uint16_t* xl = (uint16_t*)dyn;  // [xrows][xs] staged activations; row xzero is zeros
@@ -567,7 +578,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   const int HR = p.HR;
   const int h0 = min(H, cta * HR), hn = max(0, min(H, h0 + HR) - h0);
   const bool front = FEAT && p.attn;  // attention rows in place of x: x comes from the out_proj front below
-  uint32_t cx, cr;
+  uint32_t cx, cr, cx2 = 0, cr2 = 0;  // (a wide launch has up to two elements per thread)
   {
     const int r = tid / max(hn, 1), hh = tid - r * max(hn, 1);
     const uint32_t off = tid < R * hn ? (uint32_t)(r * H + h0 + hh) * 2u : OOB;
@@ -576,6 +587,13 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     cx = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.x, p.x ? (uint32_t)(R * H * 2) : 0u), (int)off, 0, 0);
     cr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.res ? p.res : p.gamma, p.res ? (uint32_t)(R * H * 2) : 0u),
                                               (int)off, 0, 0);
+    if constexpr (WIDE) {
+      const int q2 = tid + NT, r2 = q2 / max(hn, 1), hh2 = q2 - r2 * max(hn, 1);
+      const uint32_t off2 = q2 < R * hn ? (uint32_t)(r2 * H + h0 + hh2) * 2u : OOB;
+      cx2 = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.x, p.x ? (uint32_t)(R * H * 2) : 0u), (int)off2, 0, 0);
+      cr2 = __builtin_amdgcn_raw_buffer_load_b16(
+          make_rsrc(p.res ? p.res : p.gamma, p.res ? (uint32_t)(R * H * 2) : 0u), (int)off2, 0, 0);
+    }
   }
   // ---- call epoch: every workgroup counts the calls it has started, so all
   // agree on it without a shared ticket (one launch = one call per workgroup).
@@ -633,7 +651,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
     }
     return f;
   };
-  const bool is_norm = cta < R * NQ;
+  const bool is_norm = cta < (WIDE ? min(R, G / NQ) : R) * NQ;
   // Folded norm: this workgroup's K chunk of x, r and gamma (the first FCH
   // 16-byte vectors of each per thread) is loaded ahead of the weights, so
   // that it does not queue behind them; every load is issued (out-of-range
@@ -757,8 +775,9 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   if (!is_norm) w1.prime(p1_next);
 
   // ---- P0: fused residual add + RMSNorm; workgroup c < R*NQ owns slice c % NQ of row c / NQ
-  if (is_norm) {
-    const int row = cta / NQ, q = cta % NQ, SL = H / NQ;
+  // (in a wide launch, of rows c / NQ + j G / NQ, one after another)
+  if (is_norm) for (int row = cta / NQ;; row += G / NQ) {
+    const int q = cta % NQ, SL = H / NQ;
     const rsrc_t rx = make_rsrc(p.x + (size_t)row * H, (uint32_t)(H * 2));
     const rsrc_t rr = make_rsrc(p.res ? p.res + (size_t)row * H : p.x, p.res ? (uint32_t)(H * 2) : 0u);
     const rsrc_t rg = make_rsrc(p.gamma, (uint32_t)(H * 2));
@@ -864,6 +883,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         st_tag(p.gpart + row * NQ + q, __float_as_uint(t), epn);
       }
     }
+    if (!WIDE || row + G / NQ >= R) break;
+    __syncthreads();  // the next row reuses S.tmpd and S.tmpg
   }
   if (FEAT && fold) {
     // folded norm: this chunk of bf16(h * gamma), from the inputs themselves
@@ -904,7 +925,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       (void)__hip_atomic_exchange(nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (is_norm) {
-    publish(&bk->normc[cta % NQ][0], 1);
+    publish(&bk->normc[cta % NQ][0], WIDE ? (uint32_t)((R - 1 - cta / NQ) / (G / NQ) + 1) : 1u);
     w1.prime(p1_next);
   }
   TL(1);
@@ -948,28 +969,47 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   }
   TL(3);
   {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     int rb = 0, kk = 0, tt = 0;
     const int brow = (i16 < R ? i16 : xzero) * p.cs + g * 8;  // this lane's activation row in LDS
+    const int brow1 = (16 + i16 < R ? 16 + i16 : xzero) * p.cs + g * 8;  // (wide: the second tile's)
     w1.run(nu1 * TP1, p1_next, [&](const FragA& f) {
       const int t = t01 + tt;
       const u32x4 b = lds16(xc + (t < t1e ? brow + t * 32 : xzero * p.cs));
       acc = mfma(as_bf16x8(f.a), as_bf16x8(b), acc);
+      if constexpr (WIDE) {
+        const u32x4 b1 = lds16(xc + (t < t1e ? brow1 + t * 32 : xzero * p.cs));
+        acc1 = mfma(as_bf16x8(f.a), as_bf16x8(b1), acc1);
+      }
       if (++tt == TP1) {  // item done: reduce the 8 waves' partials in wave order, store the chunk's partial
         tt = 0;
         const int it = wi + kk * W1;
         ++kk;
-        S.red[rb][wave][lane] = acc;
-        acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        __syncthreads();
-        if (tid < 256) {
-          const int l = tid >> 2, qq = tid & 3;
+        if constexpr (WIDE) {  // both tiles at once (threads 256.. take the second), then a barrier
+          S.red[0][wave][lane] = acc;
+          S.red[1][wave][lane] = acc1;
+          acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+          acc1 = (f32x4){0.f, 0.f, 0.f, 0.f};
+          __syncthreads();
+          const int tl = tid >> 8, l = (tid >> 2) & 63, qq = tid & 3;
           float v = 0.f;
-          for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
-          const int row = 4 * (l >> 4) + qq, col = l & 15;
-          if (col < R) st_tag(p.part1 + (it * 16 + col) * 16 + row, __float_as_uint(v), ep);
+          for (int w = 0; w < NW; ++w) v += S.red[tl][w][l][qq];
+          const int row = 4 * (l >> 4) + qq, col = 16 * tl + (l & 15);
+          if (col < R) st_tag(p.part1 + (it * PC + col) * 16 + row, __float_as_uint(v), ep);
+          __syncthreads();
+        } else {
+          S.red[rb][wave][lane] = acc;
+          acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+          __syncthreads();
+          if (tid < 256) {
+            const int l = tid >> 2, qq = tid & 3;
+            float v = 0.f;
+            for (int w = 0; w < NW; ++w) v += S.red[rb][w][l][qq];
+            const int row = 4 * (l >> 4) + qq, col = l & 15;
+            if (col < R) st_tag(p.part1 + (it * PC + col) * 16 + row, __float_as_uint(v), ep);
+          }
+          rb ^= 1;
         }
-        rb ^= 1;
       }
     });
   }
@@ -1001,7 +1041,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         float t[NQ];
 #pragma unroll
         for (int s = 0; s < NQ; ++s)
-          if (s < S1) t[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
+          if (s < S1) t[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * PC + col) * 16 + row));
         float v = 0.f;
 #pragma unroll
         for (int s = 0; s < NQ; ++s)
@@ -1032,8 +1072,8 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 #pragma unroll
       for (int s = 0; s < NQ; ++s)
         if (s < S1) {
-          tg[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row));
-          tu[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * 16 + col) * 16 + row + 8));
+          tg[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * PC + col) * 16 + row));
+          tu[s] = __uint_as_float((uint32_t)ld_tag(p.part1 + ((u * S1 + s) * PC + col) * 16 + row + 8));
         }
       float gs = 0.f, us = 0.f;
 #pragma unroll
@@ -1272,18 +1312,25 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   {
     const uint32_t m = tid < E ? S.rowmask[tid] : 0u;
     const uint64_t bal = __ballot(m != 0u);
-    const int users = __popc(m);  // <= 16
+    const int users = __popc(m);  // <= 16 (wide: <= 32)
     int pre = 0, tot = 0;
 #pragma unroll
-    for (int b = 0; b < 5; ++b) {
+    for (int b = 0; b < (WIDE ? 6 : 5); ++b) {
       const uint64_t bb = __ballot((users >> b) & 1);
       pre += __popcll(bb & lanes_below()) << b;
       tot += __popcll(bb) << b;
     }
-    if (lane == 0) {
-      S.wcnt[wave] = __popcll(bal);
-      S.ucnt[wave] = tot;
+    // slots before this expert's in the wave (wide: one slot per 16 users)
+    int spre = 0;
+    if constexpr (WIDE) {
+      const int nse = (users + 15) >> 4;
+      const uint64_t b0 = __ballot(nse & 1), b1 = __ballot(nse >> 1);
+      spre = __popcll(b0 & lanes_below()) + 2 * __popcll(b1 & lanes_below());
+      if (lane == 0) S.wcnt[wave] = __popcll(b0) + 2 * __popcll(b1);
+    } else {
+      if (lane == 0) S.wcnt[wave] = __popcll(bal);
     }
+    if (lane == 0) S.ucnt[wave] = tot;
     __syncthreads();
     int sb = 0, ub = 0, ns = 0, nus = 0;
     for (int w = 0; w < NW; ++w) {
@@ -1296,11 +1343,18 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
       nus += b;
     }
     if (m) {
-      const int slot = sb + __popcll(bal & lanes_below());
+      const int slot = sb + (WIDE ? spre : __popcll(bal & lanes_below()));
       S.slot_expert[slot] = (int16_t)tid;
-      S.slot_mask[slot] = (uint16_t)m;
+      S.slot_mask[slot] = (typename SharedT<WIDE>::mask_t)m;
       S.slot_off[slot] = (int16_t)(ub + pre);
       S.eslot[tid] = (int16_t)slot;
+      if (WIDE && users > 16) {  // the first 16 users (in row order), then the rest
+        const uint32_t lo = m & ((1u << nth_bit(m, 16)) - 1u);
+        S.slot_mask[slot] = lo;
+        S.slot_expert[slot + 1] = (int16_t)tid;
+        S.slot_mask[slot + 1] = m & ~lo;
+        S.slot_off[slot + 1] = (int16_t)(ub + pre + 16);
+      }
     }
     if (tid == 0) {
       S.nslot = ns;
@@ -1581,17 +1635,24 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   }
   // shared down: waves split the Is/32 chunks (their first weight loads went out before top-k)
   if (Is > 0) {
-    f32x4 acc[MAX_BLK];
+    f32x4 acc[MAX_BLK], acc1[MAX_BLK];  // (wide: acc1 is the second tile of rows)
 #pragma unroll
-    for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = acc1[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
     int cu = c0s;
     const int srow = (i16 < R ? i16 : szero) * p.ss + g * 8;
+    const int srow1 = (16 + i16 < R ? 16 + i16 : szero) * p.ss + g * 8;
     if (!wse) ws.prime(sd_next);
     ws.run(CPs, sd_next, [&](const FragSD& f) {
       const u32x4 b = lds16(asl + (cu < Cs ? srow + cu * 32 : szero * p.ss));
 #pragma unroll
       for (int bl = 0; bl < MAX_BLK; ++bl)
         if (bl < nblk) acc[bl] = mfma(as_bf16x8(f.a[bl]), as_bf16x8(b), acc[bl]);
+      if constexpr (WIDE) {
+        const u32x4 b1 = lds16(asl + (cu < Cs ? srow1 + cu * 32 : szero * p.ss));
+#pragma unroll
+        for (int bl = 0; bl < MAX_BLK; ++bl)
+          if (bl < nblk) acc1[bl] = mfma(as_bf16x8(f.a[bl]), as_bf16x8(b1), acc1[bl]);
+      }
       ++cu;
     });
 #pragma unroll
@@ -1601,6 +1662,7 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
         for (int qq = 0; qq < 4; ++qq) {
           const int hh = 16 * bl + 4 * g + qq;
           if (hh < hn && i16 < R) s_shp[(wave * R + i16) * HR + hh] = acc[bl][qq];
+          if (WIDE && hh < hn && 16 + i16 < R) s_shp[(wave * R + 16 + i16) * HR + hh] = acc1[bl][qq];
         }
       }
     }
@@ -1609,93 +1671,217 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
   if (!wait_cnt<true>(p, bk, &bk->routed[0][0], 16, NRC, (uint32_t)(D * (I / 8)), false, &S.flags[4], 3, ep, (uint32_t)D))
     return;
   TL(10);
-  {  // stage the routed a [P][I] into LDS, plus its zero row
-    if (tid < P) {  // pick -> its product row: the slot's users in row order
-      const int d = S.eslot[S.ids[tid]], r = tid / K;
-      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
-    }
-    const int nr8 = P * I / 8;
-    for (int base = 0; base < nr8; base += NT * 4) {
-      u32x4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e8 = base + k * NT + tid;
-        v[k] = ld16<CP_SC1>(rs_ar, e8 < nr8 ? (uint32_t)e8 * 16u : OOB);
+  if constexpr (!WIDE) {
+    {  // stage the routed a [P][I] into LDS, plus its zero row
+      if (tid < P) {  // pick -> its product row: the slot's users in row order
+        const int d = S.eslot[S.ids[tid]], r = tid / K;
+        S.ci[tid] = (int16_t)(S.slot_off[d] + __popc((uint32_t)S.slot_mask[d] & ((1u << r) - 1u)));
       }
+      const int nr8 = P * I / 8;
+      for (int base = 0; base < nr8; base += NT * 4) {
+        u32x4 v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e8 = base + k * NT + tid;
-        if (e8 < nr8) *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+        for (int k = 0; k < 4; ++k) {
+          const int e8 = base + k * NT + tid;
+          v[k] = ld16<CP_SC1>(rs_ar, e8 < nr8 ? (uint32_t)e8 * 16u : OOB);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e8 = base + k * NT + tid;
+          if (e8 < nr8) *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+        }
       }
+      for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
+      __syncthreads();
     }
-    for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
-    __syncthreads();
-  }
-  // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
-  {
-    f32x4 acc[MAX_BLK];
+    // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
+    {
+      f32x4 acc[MAX_BLK];
 #pragma unroll
-    for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    int ju = 0, qu = 0;
-    w3.run(nsl * NP3, p3_next, [&](const FragD<F8>& f) {
-      const int d = wave + NW * ju;
-      const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
-      const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
+      for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      int ju = 0, qu = 0;
+      w3.run(nsl * NP3, p3_next, [&](const FragD<F8>& f) {
+        const int d = wave + NW * ju;
+        const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
+        const int arow = (i16 < m ? ci0 + i16 : azero) * p.as + g * 32;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int t3 = 2 * qu + t, c = 4 * t3 + g;
-        if (t3 < TI) {
-          u32x4 b[4];
+        for (int t = 0; t < 2; ++t) {
+          const int t3 = 2 * qu + t, c = 4 * t3 + g;
+          if (t3 < TI) {
+            u32x4 b[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + t3 * 128 + 8 * q : azero * p.as));
+            for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + t3 * 128 + 8 * q : azero * p.as));
 #pragma unroll
-          for (int bl = 0; bl < MAX_BLK; ++bl) {
-            if (bl < nblk) {
-              const uint32_t sb = f.s[bl][t] >> (8 * ((s3r + (16 * bl + i16) * CI + c) & 3));
-              const float sc = e8m0f(sb & 0xFFu);
+            for (int bl = 0; bl < MAX_BLK; ++bl) {
+              if (bl < nblk) {
+                const uint32_t sb = f.s[bl][t] >> (8 * ((s3r + (16 * bl + i16) * CI + c) & 3));
+                const float sc = e8m0f(sb & 0xFFu);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const bf16x8 aq = F8 ? fp8x8(f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1)],
-                                             f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1) + 1], sc)
-                                     : fp4x8(f.a[t][0][bl][q], sc);
-                acc[bl] = mfma(aq, as_bf16x8(b[q]), acc[bl]);
+                for (int q = 0; q < 4; ++q) {
+                  const bf16x8 aq = F8 ? fp8x8(f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1)],
+                                               f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1) + 1], sc)
+                                       : fp4x8(f.a[t][0][bl][q], sc);
+                  acc[bl] = mfma(aq, as_bf16x8(b[q]), acc[bl]);
+                }
               }
             }
           }
         }
+        if (++qu == NP3) {
+          qu = 0;
+#pragma unroll
+          for (int bl = 0; bl < MAX_BLK; ++bl) {
+            if (bl < nblk) {
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const int hh = 16 * bl + 4 * g + qq;
+                if (hh < hn && i16 < m) s_outp[(ci0 + i16) * HR + hh] = acc[bl][qq];
+              }
+            }
+            acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          }
+          ++ju;
+        }
+      });
+    }
+  } else {
+    if (tid < P) {  // pick -> its product row: the expert's users in row order (wide)
+      const int e = S.ids[tid], d = S.eslot[e], r = tid / K;
+      S.ci[tid] = (int16_t)(S.slot_off[d] + __popc(S.rowmask[e] & ((1u << r) - 1u)));  // over the expert's slots
+    }
+    // stage product rows [pr0, pr0 + n) of the routed a into LDS rows [0, n)
+    auto stage_a = [&](int pr0, int n) {
+      const int nr8 = n * I / 8, b8 = pr0 * I / 8;
+      for (int base = 0; base < nr8; base += NT * 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e8 = base + k * NT + tid;
+          v[k] = ld16<CP_SC1>(rs_ar, e8 < nr8 ? (uint32_t)(b8 + e8) * 16u : OOB);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e8 = base + k * NT + tid;
+          if (e8 < nr8) *(u32x4*)(al + ((e8 * 8) / I) * p.as + (e8 * 8) % I) = v[k];
+        }
       }
-      if (++qu == NP3) {
-        qu = 0;
+    };
+    // routed down: slot d on wave d % NW; frags of up to 4 column groups (slot, part)
+    {
+      f32x4 acc[MAX_BLK];
 #pragma unroll
-        for (int bl = 0; bl < MAX_BLK; ++bl) {
-          if (bl < nblk) {
+      for (int bl = 0; bl < MAX_BLK; ++bl) acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      int ju = 0, qu = 0;
+      int abase = 0;  // product row held in LDS row 0
+      auto down_use = [&](const FragD<F8>& f) {
+        const int d = wave + NW * ju;
+        const int m = __popc((uint32_t)S.slot_mask[d]), ci0 = S.slot_off[d];
+        const int arow = (i16 < m ? ci0 - abase + i16 : azero) * p.as + g * 32;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const int hh = 16 * bl + 4 * g + qq;
-              if (hh < hn && i16 < m) s_outp[(ci0 + i16) * HR + hh] = acc[bl][qq];
+        for (int t = 0; t < 2; ++t) {
+          const int t3 = 2 * qu + t, c = 4 * t3 + g;
+          if (t3 < TI) {
+            u32x4 b[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b[q] = lds16(al + (c < CI ? arow + t3 * 128 + 8 * q : azero * p.as));
+#pragma unroll
+            for (int bl = 0; bl < MAX_BLK; ++bl) {
+              if (bl < nblk) {
+                const uint32_t sb = f.s[bl][t] >> (8 * ((s3r + (16 * bl + i16) * CI + c) & 3));
+                const float sc = e8m0f(sb & 0xFFu);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const bf16x8 aq = F8 ? fp8x8(f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1)],
+                                               f.a[t][(q >> 1) & (F8 ? 1 : 0)][bl][2 * (q & 1) + 1], sc)
+                                       : fp4x8(f.a[t][0][bl][q], sc);
+                  acc[bl] = mfma(aq, as_bf16x8(b[q]), acc[bl]);
+                }
+              }
             }
           }
-          acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        ++ju;
+        if (++qu == NP3) {
+          qu = 0;
+#pragma unroll
+          for (int bl = 0; bl < MAX_BLK; ++bl) {
+            if (bl < nblk) {
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const int hh = 16 * bl + 4 * g + qq;
+                if (hh < hn && i16 < m) s_outp[(ci0 + i16) * HR + hh] = acc[bl][qq];
+              }
+            }
+            acc[bl] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          }
+          ++ju;
+        }
+      };
+      // groups of consecutive slots whose product rows fit in the azero rows
+      // of LDS; a wave's window restarts at each later group's first slot
+      for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
+      int ga = 0, jw = 0;
+      while (ga < D) {
+        const int base = S.slot_off[ga];
+        int lo = ga + 1, hi = D;  // the last slot boundary gb with slot_off[gb] - base <= azero
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (S.slot_off[mid] - base <= azero)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        const int gb = lo;
+        __syncthreads();  // the previous group's readers are done with the rows
+        stage_a(base, S.slot_off[gb] - base);
+        __syncthreads();
+        const int nw = (gb > wave ? (gb - wave + NW - 1) / NW : 0) - jw;  // this wave's slots in [ga, gb)
+        if (ga > 0) {
+          j3 = jw;
+          q3 = 0;
+          w3.prime(p3_next);
+        }
+        abase = base;
+        ju = jw;
+        qu = 0;
+        w3.run(nw * NP3, p3_next, down_use);
+        jw += nw;
+        ga = gb;
       }
-    });
+    }
   }
   TL(11);
   __syncthreads();
   // combine in a fixed order: picks in (row, k) order, then the shared part
-  if (tid < R * hn) {
-    const int r = tid / hn, hh = tid % hn, h = h0 + hh;
-    float yr = 0.f;
-    for (int k = 0; k < K; ++k) yr += S.w[r * K + k] * s_outp[S.ci[r * K + k] * HR + hh];
-    float ys = 0.f;
-    if (Is > 0)
-      for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
-    if (FEAT && p.sgate && Is > 0) ys *= S.sgw[r];
-    const uint32_t hb = f2bf(bf2f(cx) + (p.res ? bf2f(cr) : 0.f));
-    p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
-    if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
-    if (p.dbg_ys) p.dbg_ys[(size_t)r * H + h] = ys;
+  if constexpr (!WIDE) {
+    if (tid < R * hn) {
+      const int r = tid / hn, hh = tid % hn, h = h0 + hh;
+      float yr = 0.f;
+      for (int k = 0; k < K; ++k) yr += S.w[r * K + k] * s_outp[S.ci[r * K + k] * HR + hh];
+      float ys = 0.f;
+      if (Is > 0)
+        for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
+      if (FEAT && p.sgate && Is > 0) ys *= S.sgw[r];
+      const uint32_t hb = f2bf(bf2f(cx) + (p.res ? bf2f(cr) : 0.f));
+      p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
+      if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
+      if (p.dbg_ys) p.dbg_ys[(size_t)r * H + h] = ys;
+    }
+  } else {
+    auto combine = [&](int qc, uint32_t xb, uint32_t rbv) {
+      const int r = qc / hn, hh = qc % hn, h = h0 + hh;
+      float yr = 0.f;
+      for (int k = 0; k < K; ++k) yr += S.w[r * K + k] * s_outp[S.ci[r * K + k] * HR + hh];
+      float ys = 0.f;
+      if (Is > 0)
+        for (int w = 0; w < NW; ++w) ys += s_shp[(w * R + r) * HR + hh];
+      if (FEAT && p.sgate && Is > 0) ys *= S.sgw[r];
+      const uint32_t hb = f2bf(bf2f(xb) + (p.res ? bf2f(rbv) : 0.f));
+      p.out[(size_t)r * H + h] = (uint16_t)f2bf(bf2f(hb) + (yr + ys));
+      if (p.dbg_yr) p.dbg_yr[(size_t)r * H + h] = yr;
+      if (p.dbg_ys) p.dbg_ys[(size_t)r * H + h] = ys;
+    };
+    if (tid < R * hn) combine(tid, cx, cr);
+    if (WIDE && tid + NT < R * hn) combine(tid + NT, cx2, cr2);
   }
   TL(12);
 }
@@ -1706,28 +1892,37 @@ __device__ __forceinline__ void tail(const Params& p, Shared& S, char* dyn) {
 // _f kernels add the optional steps (the shared expert's gate, group-limited
 // routing).  A call runs its code once, front to back, so code it does not
 // execute still costs instruction fetches: the plain kernels carry none of it.
-#define MT_KERNEL(NAME, XL, RS, FEAT, F8)                        \
+#define MT_KERNEL(NAME, XL, RS, FEAT, F8, WIDE)                  \
   __global__ __launch_bounds__(NT, 1) void NAME(Params p) {      \
-    __shared__ Shared S;                                         \
+    __shared__ SharedT<WIDE> S;                                  \
     extern __shared__ __attribute__((aligned(16))) char s_dyn[]; \
-    tail<XL, RS, FEAT, F8>(p, S, s_dyn);                         \
+    tail<XL, RS, FEAT, F8, WIDE>(p, S, s_dyn);                   \
   }
-MT_KERNEL(moe_tail_kernel_lds, true, false, false, false)
-MT_KERNEL(moe_tail_kernel_lds_rs, true, true, false, false)
-MT_KERNEL(moe_tail_kernel_gm, false, false, false, false)
-MT_KERNEL(moe_tail_kernel_lds_f, true, false, true, false)
-MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true, false)
-MT_KERNEL(moe_tail_kernel_gm_f, false, false, true, false)
+MT_KERNEL(moe_tail_kernel_lds, true, false, false, false, false)
+MT_KERNEL(moe_tail_kernel_lds_rs, true, true, false, false, false)
+MT_KERNEL(moe_tail_kernel_gm, false, false, false, false, false)
+MT_KERNEL(moe_tail_kernel_lds_f, true, false, true, false, false)
+MT_KERNEL(moe_tail_kernel_lds_rs_f, true, true, true, false, false)
+MT_KERNEL(moe_tail_kernel_gm_f, false, false, true, false, false)
 // MXFP8 experts (E4M3 codes), without and with the optional steps
-MT_KERNEL(moe_tail_kernel_lds_8, true, false, false, true)
-MT_KERNEL(moe_tail_kernel_lds_rs_8, true, true, false, true)
-MT_KERNEL(moe_tail_kernel_gm_8, false, false, false, true)
-MT_KERNEL(moe_tail_kernel_lds_f8, true, false, true, true)
-MT_KERNEL(moe_tail_kernel_lds_rs_f8, true, true, true, true)
-MT_KERNEL(moe_tail_kernel_gm_f8, false, false, true, true)
+MT_KERNEL(moe_tail_kernel_lds_8, true, false, false, true, false)
+MT_KERNEL(moe_tail_kernel_lds_rs_8, true, true, false, true, false)
+MT_KERNEL(moe_tail_kernel_gm_8, false, false, false, true, false)
+MT_KERNEL(moe_tail_kernel_lds_f8, true, false, true, true, false)
+MT_KERNEL(moe_tail_kernel_lds_rs_f8, true, true, true, true, false)
+MT_KERNEL(moe_tail_kernel_gm_f8, false, false, true, true, false)
+// wide launches (17..32 rows), activations from global scratch
+MT_KERNEL(moe_tail_kernel_gm_w, false, false, false, false, true)
+MT_KERNEL(moe_tail_kernel_gm_wf, false, false, true, false, true)
+MT_KERNEL(moe_tail_kernel_gm_w8, false, false, false, true, true)
+MT_KERNEL(moe_tail_kernel_gm_wf8, false, false, true, true, true)
 #undef MT_KERNEL
-static const void* kernel_for(const Params& p) {
+static const void* kernel_for(const Params& p, bool wide) {
   const bool f = p.sgate || p.n_group > 1 || p.fold || p.attn;
+  if (wide) {
+    if (p.f8) return f ? (const void*)moe_tail_kernel_gm_wf8 : (const void*)moe_tail_kernel_gm_w8;
+    return f ? (const void*)moe_tail_kernel_gm_wf : (const void*)moe_tail_kernel_gm_w;
+  }
   if (p.f8) {
     if (!p.xn_lds) return f ? (const void*)moe_tail_kernel_gm_f8 : (const void*)moe_tail_kernel_gm_8;
     if (p.rsum) return f ? (const void*)moe_tail_kernel_lds_rs_f8 : (const void*)moe_tail_kernel_lds_rs_8;
@@ -1749,6 +1944,7 @@ static const void* kernel_for(const Params& p) {
 // per-pick products [picks][HR] and the shared partials [waves][rows][HR].
 struct LdsPlan {
   int xn_lds, xs, cs, as, ss, off_as, off_outp, off_shp;
+  int pa;  // routed a rows the down phase stages at once (all of them, except in a wide launch)
   size_t down, xn, chunk, dyn;
 };
 
@@ -1778,7 +1974,41 @@ static LdsPlan lds_plan(const moe_tail_config* c, int G, int TC, size_t static_b
   base = base > fr ? base : fr;
   L.xn_lds = static_bytes + (L.xn > base ? L.xn : base) <= limit;
   L.dyn = L.xn_lds && L.xn > base ? L.xn : base;
+  L.pa = (int)P;
   return L;
+}
+
+// The plan of a wide launch (R rows, 17..MAX_RW): xn stays in global scratch,
+// and the down phase stages as many routed a rows at a time as fit (at least
+// one slot's 16).  False if even that does not fit.
+static bool lds_plan_wide(const moe_tail_config* c, int R, int G, int TC, size_t static_bytes, size_t limit,
+                          LdsPlan* out) {
+  LdsPlan L;
+  const size_t P = (size_t)R * c->top_k, HR = (size_t)slice_width(c->hidden, G);
+  L.xn_lds = 0;
+  L.xs = c->hidden + mt::XPAD;
+  L.cs = TC * 32 + mt::XPAD;
+  L.as = c->inter + mt::XPAD;
+  L.ss = c->shared_inter + mt::XPAD;
+  L.xn = 0;
+  L.chunk = (R + 1) * (size_t)L.cs * 2;
+  const size_t fixed = al16((R + 1) * (size_t)L.ss * 2) + al16(P * HR * 4) + al16((size_t)mt::NW * R * HR * 4);
+  if (static_bytes + fixed >= limit) return false;
+  const size_t avail = limit - static_bytes - fixed;  // for [pa + 1][as] bf16
+  size_t pa = avail / ((size_t)L.as * 2);
+  pa = pa > 0 ? pa - 1 : 0;
+  if (pa > P) pa = P;
+  while (pa >= 16 && al16((pa + 1) * (size_t)L.as * 2) > avail) --pa;
+  if (pa < 16) return false;
+  L.pa = (int)pa;
+  L.off_as = (int)al16((pa + 1) * (size_t)L.as * 2);
+  L.off_outp = (int)(L.off_as + al16((R + 1) * (size_t)L.ss * 2));
+  L.off_shp = (int)(L.off_outp + al16(P * HR * 4));
+  L.down = L.off_shp + al16((size_t)mt::NW * R * HR * 4);
+  L.dyn = L.down > L.chunk ? L.down : L.chunk;
+  if (static_bytes + L.dyn > limit) return false;
+  *out = L;
+  return true;
 }
 
 // K chunks per router/shared block: the smallest power of two (<= 16, dividing
@@ -1811,7 +2041,10 @@ struct moe_tail {
   int S1, TC, n_rb, n_sb, Ep;
   int stall_spent;  // MOE_TAIL_DEBUG_STALL_ONCE: the first call has been launched
   int sticky;       // 1: an unread timeout makes later calls give up at once (handles); 0: each call starts clean
-  int max_rows_call;  // the caller's max_rows (cfg.max_rows is the per-launch one, at most MAX_R)
+  int max_rows_call;  // the caller's max_rows (cfg.max_rows is a narrow launch's, at most MAX_R)
+  int wide;           // calls of more than MAX_R rows run as one wide launch (else as narrow launches)
+  LdsPlan wplan;      // the wide launch's LDS plan
+  size_t wlds_dyn;
   uint64_t* xft;      // [max_rows, H/2] tagged x pairs of the out_proj front (attn_dim > 0)
   char err[256];
 };
@@ -1898,19 +2131,22 @@ struct ScratchLayout {
   size_t o_ctl, o_xn, o_xnt, o_lg, o_pt, o_gp, o_rs, o_as, o_ar, o_xf, total;
 };
 
-// Every kernel of the tail, in the order: xn staged in LDS (8), xn from global scratch (4).
-static const void* const k_all[12] = {
+// Every kernel of the tail, in the order: xn staged in LDS (8), xn from global
+// scratch (4), wide launches (4).
+static const void* const k_all[16] = {
     (const void*)mt::moe_tail_kernel_lds,    (const void*)mt::moe_tail_kernel_lds_rs,
     (const void*)mt::moe_tail_kernel_lds_f,  (const void*)mt::moe_tail_kernel_lds_rs_f,
     (const void*)mt::moe_tail_kernel_lds_8,  (const void*)mt::moe_tail_kernel_lds_rs_8,
     (const void*)mt::moe_tail_kernel_lds_f8, (const void*)mt::moe_tail_kernel_lds_rs_f8,
     (const void*)mt::moe_tail_kernel_gm,     (const void*)mt::moe_tail_kernel_gm_f,
-    (const void*)mt::moe_tail_kernel_gm_8,   (const void*)mt::moe_tail_kernel_gm_f8};
+    (const void*)mt::moe_tail_kernel_gm_8,   (const void*)mt::moe_tail_kernel_gm_f8,
+    (const void*)mt::moe_tail_kernel_gm_w,   (const void*)mt::moe_tail_kernel_gm_wf,
+    (const void*)mt::moe_tail_kernel_gm_w8,  (const void*)mt::moe_tail_kernel_gm_wf8};
 
 // Fill every field of h that depends only on the configuration and the device
 // (no allocation, no pointer into scratch yet) and the scratch layout it needs.
 static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const DevInfo& di, moe_tail_t* h,
-                                   ScratchLayout* L) {
+                                   ScratchLayout* L, bool allow_wide = true) {
   moe_tail_status st = moe_tail_check_config(cfg_in);
   if (st != MOE_TAIL_OK) return st;
   // everything below is sized per launch: at most MAX_R rows
@@ -1931,9 +2167,22 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
                 di.lds_per_block);
   if (slice_width(cfg->hidden, G) > 16 * mt::MAX_BLK)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "hidden %d too large for %d workgroups", cfg->hidden, G);
+  // more than MAX_R rows in one launch, where its LDS plan fits (not with the
+  // out_proj front, whose attention chunk is staged for MAX_R rows)
+  LdsPlan wplan;
+  memset(&wplan, 0, sizeof(wplan));
+  bool wide = false;
+  if (allow_wide && cfg_in->max_rows > mt::MAX_R && cfg_in->attn_dim == 0 &&
+      cfg_in->max_rows * cfg_in->top_k <= mt::MAX_P) {
+    HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel_gm_w));
+    wide = lds_plan_wide(cfg_in, cfg_in->max_rows, G, TC, fa.sharedSizeBytes, di.lds_per_block, &wplan);
+  }
   memset(h, 0, sizeof(*h));
   h->cfg = *cfg;
   h->max_rows_call = cfg_in->max_rows;
+  h->wide = wide;
+  h->wplan = wplan;
+  h->wlds_dyn = wide ? wplan.dyn : 0;
   h->device = dev;
   h->G = G;
   h->lds_dyn = plan.dyn;
@@ -1946,15 +2195,16 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
   h->n_sb = n_sb;
   h->Ep = (cfg->num_experts + 7) & ~7;
   h->sticky = 1;
-  const size_t R = cfg->max_rows, H = cfg->hidden, K = cfg->top_k;
-  const size_t I = cfg->inter, Is = cfg->shared_inter;
+  // rows of the widest launch; a wide launch's K-chunk partials have 32 columns
+  const size_t R = wide ? cfg_in->max_rows : cfg->max_rows, H = cfg->hidden, K = cfg->top_k;
+  const size_t I = cfg->inter, Is = cfg->shared_inter, PCOL = wide ? 32 : 16;
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
   L->o_ctl = 0;
   L->o_xn = L->o_ctl + al(sizeof(mt::Ctl));
   L->o_xnt = L->o_xn + al(R * H * 2);
   L->o_lg = L->o_xnt + al(R * H * 4);
   L->o_pt = L->o_lg + al(R * (size_t)h->Ep * 8);
-  L->o_gp = L->o_pt + al((size_t)n_it * 2048);
+  L->o_gp = L->o_pt + al((size_t)n_it * PCOL * 128);
   L->o_rs = L->o_gp + al(R * mt::NQ * 8);
   L->o_as = L->o_rs + al(R * 8);
   L->o_ar = L->o_as + al(R * (Is ? Is : 1) * 2);
@@ -1989,20 +2239,21 @@ static void place_scratch(moe_tail_t* h, const ScratchLayout& L, void* base_) {
 // (one per compute unit), which a plain launch relies on.  Call with the
 // handle's device current.
 static moe_tail_status prepare_kernels(const moe_tail_t* h, const DevInfo& di) {
-  for (int k = 0; k < 12; ++k) {
+  for (int k = 0; k < 16; ++k) {
     hipFuncAttributes fa;
     HIPCHK(nullptr, hipFuncGetAttributes(&fa, k_all[k]));
     const int lim = (int)(di.lds_per_block - fa.sharedSizeBytes);
     HIPCHK(nullptr, hipFuncSetAttribute(k_all[k], hipFuncAttributeMaxDynamicSharedMemorySize, lim));
   }
   const bool xl = h->plan.xn_lds;
-  for (int k = xl ? 0 : 8; k < (xl ? 8 : 12); ++k) {
+  for (int k = xl ? 0 : 8; k < (h->wide ? 16 : xl ? 8 : 12); ++k) {
+    if (xl && k >= 8 && k < 12) continue;
+    const size_t dyn = k >= 12 ? h->wlds_dyn : h->lds_dyn;
     int nb = 0;
-    HIPCHK(nullptr, hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_all[k], mt::NT, h->lds_dyn));
+    HIPCHK(nullptr, hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_all[k], mt::NT, dyn));
     if (nb < 1)
       return fail(nullptr, MOE_TAIL_EUNSUPPORTED,
-                  "a workgroup of %d threads with %zu B of dynamic LDS does not fit on a compute unit", mt::NT,
-                  h->lds_dyn);
+                  "a workgroup of %d threads with %zu B of dynamic LDS does not fit on a compute unit", mt::NT, dyn);
   }
   return MOE_TAIL_OK;
 }
@@ -2049,10 +2300,13 @@ extern "C" moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// One launch over rows <= MAX_R.
+// One launch: narrow over rows <= MAX_R, or wide over more (handles with wide set).
 static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
   const moe_tail_config& c = h->cfg;
-  if (rows < 1 || rows > c.max_rows) return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, c.max_rows);
+  const bool wide = rows > c.max_rows && h->wide;
+  const int lim = wide ? h->max_rows_call : c.max_rows;
+  if (rows < 1 || rows > lim) return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, lim);
+  const LdsPlan& pl = wide ? h->wplan : h->plan;
   // x, or attention rows for the out_proj front (checked by the caller)
   const void* req[] = {a->attn ? a->attn : a->x, a->gamma, a->router_w, a->w13_q, a->w13_s, a->w2_q, a->w2_s, a->out};
   const char* names[] = {"x", "gamma", "router_w", "w13_q", "w13_s", "w2_q", "w2_s", "out"};
@@ -2090,11 +2344,11 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.fold = c.fold_norm;
   p.shuf = c.w13_layout == 1;
   p.G = h->G;
-  p.xn_lds = h->plan.xn_lds;
+  p.xn_lds = pl.xn_lds;
   // reader-side router sums when each thread then loads at most 8 partials
   p.rsum = p.xn_lds && rows * c.num_experts * h->S1 <= 8192 && rows * c.num_experts <= mt::RED_FLOATS;
-  p.xs = h->plan.xs;
-  p.cs = h->plan.cs;
+  p.xs = pl.xs;
+  p.cs = pl.cs;
   p.n_rb = h->n_rb;
   p.n_sb = h->n_sb;
   {  // the norm's workgroups take no router/shared items when they are few
@@ -2109,14 +2363,14 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   p.S1 = h->S1;
   p.TC = h->TC;
   p.Ep = h->Ep;
-  p.as = h->plan.as;
-  p.ss = h->plan.ss;
-  p.off_as = h->plan.off_as;
-  p.off_outp = h->plan.off_outp;
-  p.off_shp = h->plan.off_shp;
-  p.xzero = c.max_rows;
-  p.azero = c.max_rows * c.top_k;
-  p.szero = c.max_rows;
+  p.as = pl.as;
+  p.ss = pl.ss;
+  p.off_as = pl.off_as;
+  p.off_outp = pl.off_outp;
+  p.off_shp = pl.off_shp;
+  p.xzero = wide ? h->max_rows_call : c.max_rows;
+  p.azero = wide ? pl.pa : c.max_rows * c.top_k;
+  p.szero = p.xzero;
   p.eps = (double)c.eps;
   p.deadline_ticks = h->deadline_ticks;
   p.debug_flags = c.debug_flags & MOE_TAIL_DEBUG_STALL;
@@ -2165,8 +2419,9 @@ static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_ar
   // an otherwise idle device; a wait that is never met (another kernel holding
   // compute units) ends at its deadline with ETIMEOUT instead of hanging.
   void* kargs[] = {&p};
-  const void* kern = mt::kernel_for(p);
-  const hipError_t e = hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, h->lds_dyn, (hipStream_t)stream);
+  const void* kern = mt::kernel_for(p, wide);
+  const hipError_t e =
+      hipLaunchKernel(kern, dim3(h->G), dim3(mt::NT), kargs, wide ? h->wlds_dyn : h->lds_dyn, (hipStream_t)stream);
   if (e != hipSuccess) return fail(h, MOE_TAIL_EHIP, "kernel launch: %s", hipGetErrorString(e));
   return MOE_TAIL_OK;
 }
@@ -2183,9 +2438,10 @@ extern "C" moe_tail_status moe_tail_run(moe_tail_t* h, int32_t rows, const moe_t
     if (!aligned(a->attn, 16) || !aligned(a->w_o, 16)) return fail(h, MOE_TAIL_EINVAL, "attn/w_o are not 16-byte aligned");
     if (h->cfg.fold_norm) return fail(h, MOE_TAIL_EUNSUPPORTED, "the folded norm does not take attn (it reads x by chunks)");
   }
-  if (rows <= mt::MAX_R) return run_launch(h, rows, a, stream);
-  // More rows than one launch's MFMA columns: balanced row ranges, one
-  // launch each, in order on the stream (each streams its own experts)
+  if (rows <= mt::MAX_R || h->wide) return run_launch(h, rows, a, stream);
+  // More rows than a narrow launch's MFMA columns, on a handle without the
+  // wide launch: balanced row ranges, one launch each, in order on the
+  // stream (each streams its own experts)
   const int n = (rows + mt::MAX_R - 1) / mt::MAX_R;
   const size_t H = h->cfg.hidden, E = h->cfg.num_experts, K = h->cfg.top_k;
   for (int i = 0; i < n; ++i) {
@@ -2266,6 +2522,7 @@ struct NoallocDev {
   DevInfo info;
   size_t lds_ready;  // largest dynamic LDS size prepared so far, per kernel family (0: none)
   size_t lds_ready_gm;
+  size_t lds_ready_w;
 };
 NoallocDev g_noalloc[NOALLOC_MAX_DEV];
 std::mutex g_noalloc_mu;
@@ -2295,14 +2552,19 @@ extern "C" moe_tail_status moe_tail_run_noalloc(const moe_tail_config* cfg, int3
       d.ready = 1;
     }
     if ((st = plan_handle(cfg, dev, d.info, &h, &L)) != MOE_TAIL_OK) return st;
+    // a wide launch's scratch (32-column partials, all rows) may not fit where
+    // narrow launches' does: then calls above 16 rows run as narrow launches
+    if (L.total > sizeof(scratch) && h.wide && (st = plan_handle(cfg, dev, d.info, &h, &L, false)) != MOE_TAIL_OK)
+      return st;
     if (L.total > sizeof(scratch))
       return fail(nullptr, MOE_TAIL_EINVAL, "this configuration needs %zu B of scratch; moe_tail_run_noalloc has %zu",
                   L.total, sizeof(scratch));
     // the residency check passed at this dynamic LDS size or a larger one
     size_t& done = h.plan.xn_lds ? d.lds_ready : d.lds_ready_gm;
-    if (h.lds_dyn > done || !done) {
+    if (h.lds_dyn > done || !done || (h.wide && (h.wlds_dyn > d.lds_ready_w || !d.lds_ready_w))) {
       if ((st = prepare_kernels(&h, d.info)) != MOE_TAIL_OK) return st;
       done = h.lds_dyn > done ? h.lds_dyn : done;
+      if (h.wide && h.wlds_dyn > d.lds_ready_w) d.lds_ready_w = h.wlds_dyn;
     }
     place_scratch(&h, L, d.ptr);
   }

@@ -169,10 +169,19 @@ moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
  * return without synchronising.  The call is the whole tail in one persistent
  * launch ("[AMD] integrate kimi k3 monokernel", K2 commit text, Motivation:
  * the layer tail as a single launch; Kernel checks: graph replays of mixed
- * widths give the eager bits).  1 <= rows <= max_rows.  One launch takes up
- * to 16 rows (its MFMA columns); more rows (MTP verify batches) run as
- * ceil(rows / 16) launches over balanced row ranges, in order on the stream,
- * each de-duplicating and streaming its own experts.  Graph-capturable:
+ * widths give the eager bits).  1 <= rows <= max_rows.  Up to 16 rows run
+ * as a narrow launch (one 16-column MFMA tile of rows).  More rows (MTP
+ * verify batches; the pages' launch falls back above concurrency 16, K2
+ * commit text, section Speed) run as one wide launch when the handle allows
+ * it: max_rows * top_k <= 512, attn_dim == 0 and its LDS plan fits the
+ * device.  A wide launch de-duplicates experts across all rows, so each
+ * distinct expert streams once per call; where rows are MFMA columns (router
+ * and shared gate/up, shared down) a weight load feeds two 16-column tiles,
+ * and an expert picked by more than 16 rows runs as one slot per 16 of them
+ * (its weights are read once per slot, the second time mostly from L2).
+ * Otherwise such calls run as ceil(rows / 16) narrow launches over balanced
+ * row ranges, in order on the stream, each streaming its own experts.  A
+ * row's outputs are the same bits at every width.  Graph-capturable:
  * the handle's per-call epoch lives in device memory, so replays need no
  * host work.  Calls on one handle must be ordered (one stream at a time).
  * Argument errors are returned synchronously and nothing is enqueued; a
@@ -198,7 +207,9 @@ void moe_tail_destroy(moe_tail_t* h);
 
 /* Scratch bytes available to moe_tail_run_noalloc (4 MiB): enough for every
  * configuration up to 16 rows per launch with H <= 8192, E <= 512, K <= 10,
- * I <= 256 and Is <= 512 (at most 3.3 MB); larger ones are refused. */
+ * I <= 256 and Is <= 512 (at most 3.3 MB); larger ones are refused.  Where a
+ * wide launch's scratch (more than 16 rows) does not fit, calls above 16 rows
+ * run as narrow launches instead. */
 #define MOE_TAIL_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* For callers that cannot allocate device memory: code under HIP graph

@@ -96,7 +96,7 @@ def test_graph_replay_of_mixed_row_counts(max_rows):
 
 
 def test_graph_replay_above_16_rows():
-    """Calls of more than 16 rows (two launches each) captured in one graph
+    """Calls of more than 16 rows (one wide launch each) captured in one graph
     with a 5-row call between them: every replay equals the eager results."""
     t = pytest.importorskip("torch")
     cfg = synth.CONFIGS["c1"].with_rows(24)

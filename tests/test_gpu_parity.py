@@ -272,9 +272,10 @@ def test_parity_every_option_together(name, rows, n_group, topk_group):
 
 @pytest.mark.parametrize("name,rows,max_rows", [("c1", 32, 32), ("c3", 20, 24), ("c0", 17, 32)])
 def test_parity_above_16_rows(name, rows, max_rows):
-    """More rows than one launch's 16 MFMA columns (MTP verify batches) run as
-    balanced row ranges, one launch each: parity with the oracle on every row,
-    and the first range equals a call on those rows alone, bit for bit."""
+    """More rows than a narrow launch's 16 MFMA columns (MTP verify batches)
+    run as one wide launch: parity with the oracle on every row, and the first
+    rows (the first range of the narrow-launch split) equal a call on those
+    rows alone, bit for bit."""
     cfg = synth.CONFIGS[name].with_rows(rows)
     _say("rows", name, rows, "max_rows", max_rows)
     w = weights(name)
