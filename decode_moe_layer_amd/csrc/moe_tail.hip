@@ -362,6 +362,21 @@ struct Window {
       }
     }
   }
+  // The same for a window that has already used m items, m = S mod (D + 1):
+  // its next item to use is in slot S.  Runs one after another continue the
+  // one source without emptying the window in between.
+  template <int S, class NextF, class UseF>
+  __device__ __forceinline__ void run_rot(int n, NextF next, UseF use) {
+    for (int base = 0; base < n; base += D + 1) {
+#pragma unroll
+      for (int j = 0; j <= D; ++j) {
+        if (base + j < n) {
+          buf[(S + j + D) % (D + 1)] = next();
+          use(buf[(S + j) % (D + 1)]);
+        }
+      }
+    }
+  }
 };
 
 // -------------------------------------------------------- cross-CTA sync --
@@ -1817,9 +1832,10 @@ __device__ __forceinline__ void tail(const Params& p, SharedT<WIDE>& S, char* dy
         }
       };
       // groups of consecutive slots whose product rows fit in the azero rows
-      // of LDS; a wave's window restarts at each later group's first slot
-      for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
-      int ga = 0, jw = 0;
+      // of LDS (which overlap the shared a, no longer read); each wave's
+      // window runs on across the groups: the frag in flight at a group's end
+      // is the wave's first of the next group
+      int ga = 0, jw = 0, used = 0;
       while (ga < D) {
         const int base = S.slot_off[ga];
         int lo = ga + 1, hi = D;  // the last slot boundary gb with slot_off[gb] - base <= azero
@@ -1831,19 +1847,18 @@ __device__ __forceinline__ void tail(const Params& p, SharedT<WIDE>& S, char* dy
             hi = mid - 1;
         }
         const int gb = lo;
-        __syncthreads();  // the previous group's readers are done with the rows
+        __syncthreads();  // the previous group's readers (or the shared down) are done with the rows
+        if (ga == 0)
+          for (int c = tid * 8; c < p.as; c += NT * 8) *(u32x4*)(al + azero * p.as + c) = (u32x4){0u, 0u, 0u, 0u};
         stage_a(base, S.slot_off[gb] - base);
         __syncthreads();
         const int nw = (gb > wave ? (gb - wave + NW - 1) / NW : 0) - jw;  // this wave's slots in [ga, gb)
-        if (ga > 0) {
-          j3 = jw;
-          q3 = 0;
-          w3.prime(p3_next);
-        }
         abase = base;
-        ju = jw;
-        qu = 0;
-        w3.run(nw * NP3, p3_next, down_use);
+        if (used & 1)
+          w3.template run_rot<1>(nw * NP3, p3_next, down_use);
+        else
+          w3.template run_rot<0>(nw * NP3, p3_next, down_use);
+        used += nw * NP3;
         jw += nw;
         ga = gb;
       }
@@ -1992,17 +2007,21 @@ static bool lds_plan_wide(const moe_tail_config* c, int R, int G, int TC, size_t
   L.ss = c->shared_inter + mt::XPAD;
   L.xn = 0;
   L.chunk = (R + 1) * (size_t)L.cs * 2;
-  const size_t fixed = al16((R + 1) * (size_t)L.ss * 2) + al16(P * HR * 4) + al16((size_t)mt::NW * R * HR * 4);
-  if (static_bytes + fixed >= limit) return false;
-  const size_t avail = limit - static_bytes - fixed;  // for [pa + 1][as] bf16
+  // the routed a [pa + 1][as] and the shared a [R + 1][ss] share the first
+  // region: the shared down is done before the routed a is staged
+  const size_t fixed = al16(P * HR * 4) + al16((size_t)mt::NW * R * HR * 4);
+  const size_t sa = al16((R + 1) * (size_t)L.ss * 2);
+  if (static_bytes + fixed + sa > limit) return false;
+  const size_t avail = limit - static_bytes - fixed;
   size_t pa = avail / ((size_t)L.as * 2);
   pa = pa > 0 ? pa - 1 : 0;
   if (pa > P) pa = P;
   while (pa >= 16 && al16((pa + 1) * (size_t)L.as * 2) > avail) --pa;
   if (pa < 16) return false;
   L.pa = (int)pa;
-  L.off_as = (int)al16((pa + 1) * (size_t)L.as * 2);
-  L.off_outp = (int)(L.off_as + al16((R + 1) * (size_t)L.ss * 2));
+  const size_t ra = al16((pa + 1) * (size_t)L.as * 2);
+  L.off_as = 0;
+  L.off_outp = (int)(ra > sa ? ra : sa);
   L.off_shp = (int)(L.off_outp + al16(P * HR * 4));
   L.down = L.off_shp + al16((size_t)mt::NW * R * HR * 4);
   L.dyn = L.down > L.chunk ? L.down : L.chunk;
