@@ -36,6 +36,8 @@ MALL_BYTES = 256 * 2**20
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "moe_tail_kernel_c2_8rows_hbm_traffic.txt")
 KERNEL_SOURCES = (os.path.join(ROOT, "decode_moe_layer_amd", "csrc", "moe_tail.hip"),
+                  os.path.join(ROOT, "decode_moe_layer_amd", "csrc", "moe_tail_device.h"),
+                  os.path.join(ROOT, "decode_moe_layer_amd", "csrc", "moe_tail_wide.hip"),
                   os.path.join(ROOT, "include", "moe_tail.h"))
 
 

@@ -5,7 +5,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "moe_tail.hip")
+# the narrow kernels and the host code; the wide kernels in a code object of their own
+SRCS = [os.path.join(HERE, "csrc", "moe_tail.hip"), os.path.join(HERE, "csrc", "moe_tail_wide.hip")]
+SRC = SRCS[0]
 LIB = os.path.join(HERE, "libmoe_tail.so")
 
 FLAGS = [
@@ -17,7 +19,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", *FLAGS, SRC, "-o", tmp]
+    cmd = ["hipcc", *FLAGS, *SRCS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
