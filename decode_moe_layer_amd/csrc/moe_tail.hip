@@ -19,10 +19,13 @@
 //           (chunk-ordered fp32 partials: "Split the Kimi3 AttnRes mix across
 //           CTAs for decode rows", flare PR 11, design section)
 //
-// A call of more than 16 rows runs as launches over balanced row ranges of
-// at most 16 (a launch's MFMA columns).  With attention rows in place of x,
-// the out_proj front (K2 commit text, Motivation and Modifications) runs
-// first as a launch of its own: x = bf16(attn . W_o^T), summed in double.
+// A call of 17..32 rows runs as one wide launch (moe_tail_wide.hip): two
+// 16-column MFMA tiles where rows are columns, one slot per 16 users of an
+// expert, so experts are still de-duplicated across all rows; handles that
+// cannot take it run such calls as narrow launches of at most 16 rows.  With
+// attention rows in place of x, the out_proj front (K2 commit text,
+// Motivation and Modifications) runs first in the same launch:
+// x = bf16(attn . W_o^T), summed in double.
 //
 // Optional steps (separate kernel variants): the shared expert's output scaled
 // by a sigmoid gate of the normed row (K2 commit text, Kernel Replacement), and
