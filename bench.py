@@ -17,6 +17,7 @@ expert, gamma, activations in and out) over the measured time per call.
 import argparse
 import dataclasses
 import hashlib
+import re
 import json
 import os
 import sys
@@ -42,10 +43,17 @@ KERNEL_SOURCES = (os.path.join(ROOT, "decode_moe_layer_amd", "csrc", "moe_tail.h
 
 
 def kernel_source_hash():
+    """SHA-256 of the kernel and ABI sources with comments and blank lines
+    removed: a comment-only edit keeps the measured traffic valid, any change
+    to the code does not."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 

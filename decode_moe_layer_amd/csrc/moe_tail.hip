@@ -1,6 +1,6 @@
 // Fused decode MoE layer tail for MI355X (gfx950): one persistent launch.
 //
-// Steps (one tensor-parallel rank's shard, 1..16 rows), after "[AMD]
+// Steps (one tensor-parallel rank's shard, 1..32 rows), after "[AMD]
 // integrate kimi k3 monokernel" (sglang PR 43481), K2 commit text, sections
 // Motivation and "Kernel Replacement":
 //   norm    h = bf16(x + residual); xn = bf16(h * rstd * gamma), rstd in fp64
@@ -48,7 +48,7 @@
 // for decode rows", design section: per-call tags in the exchanged words).
 //
 // GEMV tiles use v_mfma_f32_16x16x32_bf16: weights are the A operand (16
-// rows), activations the B operand (up to 16 rows as columns), staged in LDS.
+// rows), activations the B operand (16 rows as columns per tile), staged in LDS.
 // MXFP4 codes are dequantised exactly to bf16 with v_cvt_scalef32_pk_bf16_fp4
 // (E2M1 x 2^(s-127) is exact in bf16 for the scales in range), so every
 // product is exact and accumulation is fp32.  A lane's 16-byte weight load is
