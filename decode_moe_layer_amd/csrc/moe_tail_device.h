@@ -455,6 +455,11 @@ struct FragQB {  // one column group (one 16-byte load of MXFP4 codes, two of MX
   uint32_t s;
   u32x4 b[4];
 };
+struct FragQB2 {  // MXFP4, two units of one slot: a column group's codes of both, one set of B fragments
+  u32x4 a[2];
+  uint32_t s[2];
+  u32x4 b[4];
+};
 template <bool F8>
 struct FragD {  // down: 2 column groups x both row blocks (x 2 halves for MXFP8), with their scale dwords
   u32x4 a[2][F8 ? 2 : 1][MAX_BLK];
@@ -1336,7 +1341,11 @@ __device__ __forceinline__ void tail(const Params& p, SharedT<WIDE>& S, char* dy
 
   // ---- P2: routed gate/up units (slot, 8 intermediate indices), waves split K
   {
-    const int UB = I / 8, n_p2 = D * UB;
+    // DU: with activations from global memory (MXFP4), a work unit is two
+    // units (blocks b, b + 1 of one slot) whose two weight tiles share each
+    // activation load, which doubles the weight bytes a wave keeps in flight
+    constexpr bool DU = !XL && !F8;
+    const int UB = I / 8, UW = DU ? UB / 2 : UB, n_p2 = D * UW;
     const int T2 = H / 128, TP2 = (T2 + NW - 1) / NW, t02 = wave * TP2;
     // Units go round-robin from workgroup off2 on: the workgroups before it
     // reach this phase last (the norm's, or those with one more router/shared
@@ -1441,62 +1450,124 @@ __device__ __forceinline__ void tail(const Params& p, SharedT<WIDE>& S, char* dy
       });
     } else {
       // activations from global memory: one column group per frag, with its B fragments
-      int k2 = 0, t2 = t02;
-      rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
-      uint32_t qoff = 0, soff = 0, boff = OOB, qst = F8 ? 128u : 64u;
-      auto p2_unit = [&]() {
-        const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
-        const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
-        rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
-        rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
-        const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
-        const bool sh = !F8 && p.shuf;  // unit-blocked MXFP4 layout
-        qoff = sh ? (uint32_t)(b * T2 * 1024 + lane * 16) : (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
-        qst = sh ? 1024u : (F8 ? 128u : 64u);
-        soff = (uint32_t)(wrow * (H / 32));
-        const uint32_t mask = S.slot_mask[d];
-        boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
-      };
-      if (nu2) p2_unit();
-      auto p2_next = [&]() {
-        FragQB<F8> f;
-        const bool v = k2 < nu2 && t2 < T2;
+      if constexpr (DU) {
+        // work unit w = (slot d, pair bp): units (d, 2 bp) and (d, 2 bp + 1)
+        int k2 = 0, t2 = t02;
+        rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
+        uint32_t qoff0 = 0, qoff1 = 0, soff0 = 0, soff1 = 0, boff = OOB, qst = 64u;
+        auto p2_unit = [&]() {
+          const int w = u0 + k2 * G, d = w / UW, b = 2 * (w - d * UW);
+          const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
+          rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
+          rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
+          const int wrow0 = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8), wrow1 = wrow0 + 8;
+          const bool sh = p.shuf;  // unit-blocked MXFP4 layout
+          qoff0 = sh ? (uint32_t)(b * T2 * 1024 + lane * 16) : (uint32_t)(wrow0 * RB13 + g * 16);
+          qoff1 = sh ? qoff0 + (uint32_t)(T2 * 1024) : (uint32_t)(wrow1 * RB13 + g * 16);
+          qst = sh ? 1024u : 64u;
+          soff0 = (uint32_t)(wrow0 * (H / 32));
+          soff1 = (uint32_t)(wrow1 * (H / 32));
+          const uint32_t mask = S.slot_mask[d];
+          boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
+        };
+        if (nu2) p2_unit();
+        auto p2_next = [&]() {
+          FragQB2 f;
+          const bool v = k2 < nu2 && t2 < T2;
+          f.a[0] = ld16<CP_W>(rq2, v ? qoff0 + (uint32_t)t2 * qst : OOB);
+          f.a[1] = ld16<CP_W>(rq2, v ? qoff1 + (uint32_t)t2 * qst : OOB);
+          f.s[0] = ld4<CP_W>(rsc2, v ? soff0 + (uint32_t)t2 * 4u : OOB);
+          f.s[1] = ld4<CP_W>(rsc2, v ? soff1 + (uint32_t)t2 * 4u : OOB);
 #pragma unroll
-        for (int j = 0; j < (F8 ? 2 : 1); ++j)
-          f.a[j] = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * qst + (uint32_t)j * 16u : OOB);
-        f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
+          for (int q = 0; q < 4; ++q)
+            f.b[q] = ld16<CP_SC1>(rs_xn, (v && boff != OOB) ? boff + (uint32_t)(t2 * 256 + 16 * q) : OOB);
+          if (++t2 == t02 + TP2) {
+            t2 = t02;
+            if (++k2 < nu2) p2_unit();
+          }
+          return f;
+        };
+        Window<D_FP4_G, FragQB2> w2;
+        w2.prime(p2_next);
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        int kk = 0, tt = 0;
+        if (nu2 && TL_ON) TL(13);
+        w2.run(nu2 * TP2, p2_next, [&](const FragQB2& f) {
+          const float sc0 = e8m0f((f.s[0] >> (8 * g)) & 0xFFu), sc1 = e8m0f((f.s[1] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          f.b[q] = ld16<CP_SC1>(rs_xn, (v && boff != OOB) ? boff + (uint32_t)(t2 * 256 + 16 * q) : OOB);
-        if (++t2 == t02 + TP2) {
-          t2 = t02;
-          if (++k2 < nu2) p2_unit();
-        }
-        return f;
-      };
-      Window<D_FP4_G, FragQB<F8>> w2;
-      w2.prime(p2_next);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      int kk = 0, tt = 0;
-      if (nu2 && TL_ON) TL(13);
-      w2.run(nu2 * TP2, p2_next, [&](const FragQB<F8>& f) {
-        const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
+          for (int q = 0; q < 4; ++q) {
+            acc0 = mfma(fp4x8(f.a[0][q], sc0), as_bf16x8(f.b[q]), acc0);
+            acc1 = mfma(fp4x8(f.a[1][q], sc1), as_bf16x8(f.b[q]), acc1);
+          }
+          if (++tt == TP2) {
+            tt = 0;
+            const int w = u0 + kk * G, d = w / UW, u = d * UB + 2 * (w - d * UW);
+            p2_reduce(acc0, u);
+            p2_reduce(acc1, u + 1);
+            acc0 = (f32x4){0.f, 0.f, 0.f, 0.f};
+            acc1 = (f32x4){0.f, 0.f, 0.f, 0.f};
+            if (kk < 8) TL(14 + kk);
+            ++kk;
+          }
+        });
+      } else {
+        int k2 = 0, t2 = t02;
+        rsrc_t rq2 = rs_xn, rsc2 = rs_xn;
+        uint32_t qoff = 0, soff = 0, boff = OOB, qst = F8 ? 128u : 64u;
+        auto p2_unit = [&]() {
+          const int u = u0 + k2 * G, d = u / UB, b = u - d * UB;
+          const int e = __builtin_amdgcn_readfirstlane(S.slot_expert[d]);  // uniform: scalar descriptors
+          rq2 = make_rsrc(p.w13q + e * S13, (uint32_t)S13);
+          rsc2 = make_rsrc(p.w13s + e * S13s, (uint32_t)S13s);
+          const int wrow = i16 < 8 ? b * 8 + i16 : I + b * 8 + (i16 - 8);
+          const bool sh = !F8 && p.shuf;  // unit-blocked MXFP4 layout
+          qoff = sh ? (uint32_t)(b * T2 * 1024 + lane * 16) : (uint32_t)(wrow * RB13 + g * (F8 ? 32 : 16));
+          qst = sh ? 1024u : (F8 ? 128u : 64u);
+          soff = (uint32_t)(wrow * (H / 32));
+          const uint32_t mask = S.slot_mask[d];
+          boff = i16 < __popc(mask) ? (uint32_t)(nth_bit(mask, i16) * H + g * 32) * 2u : OOB;
+        };
+        if (nu2) p2_unit();
+        auto p2_next = [&]() {
+          FragQB<F8> f;
+          const bool v = k2 < nu2 && t2 < T2;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x8 aq = F8 ? fp8x8(f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1)], f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1) + 1], sc)
-                               : fp4x8(f.a[0][q], sc);
-          acc = mfma(aq, as_bf16x8(f.b[q]), acc);
-        }
-        if (++tt == TP2) {
-          tt = 0;
-          p2_reduce(acc, u0 + kk * G);
-          acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-          if (kk < 8) TL(14 + kk);
-          ++kk;
-        }
-      });
+          for (int j = 0; j < (F8 ? 2 : 1); ++j)
+            f.a[j] = ld16<CP_W>(rq2, v ? qoff + (uint32_t)t2 * qst + (uint32_t)j * 16u : OOB);
+          f.s = ld4<CP_W>(rsc2, v ? soff + (uint32_t)t2 * 4u : OOB);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            f.b[q] = ld16<CP_SC1>(rs_xn, (v && boff != OOB) ? boff + (uint32_t)(t2 * 256 + 16 * q) : OOB);
+          if (++t2 == t02 + TP2) {
+            t2 = t02;
+            if (++k2 < nu2) p2_unit();
+          }
+          return f;
+        };
+        Window<D_FP4_G, FragQB<F8>> w2;
+        w2.prime(p2_next);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int kk = 0, tt = 0;
+        if (nu2 && TL_ON) TL(13);
+        w2.run(nu2 * TP2, p2_next, [&](const FragQB<F8>& f) {
+          const float sc = e8m0f((f.s >> (8 * g)) & 0xFFu);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x8 aq = F8 ? fp8x8(f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1)], f.a[(q >> 1) & (F8 ? 1 : 0)][2 * (q & 1) + 1], sc)
+                                 : fp4x8(f.a[0][q], sc);
+            acc = mfma(aq, as_bf16x8(f.b[q]), acc);
+          }
+          if (++tt == TP2) {
+            tt = 0;
+            p2_reduce(acc, u0 + kk * G);
+            acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+            if (kk < 8) TL(14 + kk);
+            ++kk;
+          }
+        });
+      }
     }
-    if (nu2) publish(&bk->routed[cta % NRC][0], (uint32_t)nu2);
+    if (nu2) publish(&bk->routed[cta % NRC][0], (uint32_t)(DU ? 2 * nu2 : nu2));
   }
   TL(8);
 
