@@ -91,6 +91,23 @@ def test_noalloc_across_configurations():
         _same(run_noalloc(cfg, rows, dw, x, r), refs[name], name)
 
 
+@pytest.mark.parametrize("name,rows", [("c0", 24), ("c1", 32)])
+def test_noalloc_above_16_rows(name, rows):
+    """More than 16 rows without a handle: c0's wide-launch scratch fits the
+    static array, c1's at 32 rows does not, so that call runs as narrow
+    launches.  Both give the handle's (wide launch) bits."""
+    cfg = synth.CONFIGS[name].with_rows(rows)
+    _say("noalloc above 16 rows", name, rows)
+    w = weights(name)
+    x, r, _ = gapped_rows(cfg, w)
+    dw = device_weights(name)
+    h = handle_for(cfg, max_rows=32)
+    ref = run(h, cfg, dw, x, r)
+    assert h.get_error() == binding.OK
+    h.close()
+    _same(run_noalloc(cfg, 32, dw, x, r), ref, "%s %d rows" % (name, rows))
+
+
 def test_noalloc_in_a_captured_graph():
     t = pytest.importorskip("torch")
     cfg = synth.CONFIGS["c1"].with_rows(8)
