@@ -75,7 +75,8 @@ struct Params {
   int xs, as, ss;                 // LDS row strides (bf16 elements): xn, routed a, shared a
   int cs;                         // LDS row stride of the router/shared phase's xn chunk
   int off_as, off_outp, off_shp;  // byte offsets in dynamic LDS (down phase)
-  int xzero, azero, szero;        // indices of the all-zero LDS rows (inactive MFMA columns)
+  int xzero, azero, szero;        // indices of the all-zero LDS rows (inactive MFMA columns); a wide
+                                  // launch stages up to azero routed a rows at a time
   int n_rb, n_sb;                 // router blocks (16 experts), shared blocks (8 gate + 8 up rows)
   int nn1;                        // leading workgroups that take no router/shared items (the norm's, at few rows)
   int S1, TC;                     // K chunks per block, 32-column groups per chunk
@@ -112,7 +113,7 @@ struct Params {
   uint16_t* xn;
   uint64_t* xnt;    // [R][H/2] tagged xn pairs (this call's K-chunk readers)
   uint64_t* lgt;    // [R][Ep] tagged fp32 logits
-  uint64_t* part1;  // [blocks * S1][16][16] tagged fp32 K-chunk partial sums
+  uint64_t* part1;  // [blocks * S1][16 or, wide, 32 rows][16] tagged fp32 K-chunk partial sums
   uint64_t* gpart;  // [R][NQ] tagged fp32 partial dots of the shared gate, one per norm slice
   uint64_t* rstdt;  // [R] tagged fp32 rstd of each row (folded norm)
   uint64_t* xft;    // [R][H/2] tagged x pairs computed by the out_proj front, one slice per workgroup
