@@ -220,6 +220,7 @@ struct moe_tail {
   int sticky;       // 1: an unread timeout makes later calls give up at once (handles); 0: each call starts clean
   int max_rows_call;  // the caller's max_rows (cfg.max_rows is a narrow launch's, at most MAX_R)
   int wide;           // calls of more than MAX_R rows run as one wide launch (else as narrow launches)
+  int wide_only;      // the narrow plan does not fit: every call is a wide launch
   LdsPlan wplan;      // the wide launch's LDS plan
   size_t wlds_dyn;
   uint64_t* xft;      // [max_rows, H/2] tagged x pairs of the out_proj front (attn_dim > 0)
@@ -339,25 +340,29 @@ static moe_tail_status plan_handle(const moe_tail_config* cfg_in, int dev, const
   if ((n_it + G - 1) / G > mt::MAX_ITEMS1)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "%d router/shared items exceed %d per workgroup", n_it, mt::MAX_ITEMS1);
   const LdsPlan plan = lds_plan(cfg, G, TC, fa.sharedSizeBytes, di.lds_per_block);
-  if (plan.dyn + fa.sharedSizeBytes > di.lds_per_block)
-    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", plan.dyn + fa.sharedSizeBytes,
-                di.lds_per_block);
+  const bool narrow_fits = plan.dyn + fa.sharedSizeBytes <= di.lds_per_block;
   if (slice_width(cfg->hidden, G) > 16 * mt::MAX_BLK)
     return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "hidden %d too large for %d workgroups", cfg->hidden, G);
-  // more than MAX_R rows in one launch, where its LDS plan fits (not with the
-  // out_proj front, whose attention chunk is staged for MAX_R rows)
+  // The wide launch: more than MAX_R rows in one launch, or every call where
+  // the narrow plan does not fit (its routed a staged in groups), when its
+  // own plan fits (not with the out_proj front, whose attention chunk is
+  // staged for MAX_R rows)
   LdsPlan wplan;
   memset(&wplan, 0, sizeof(wplan));
   bool wide = false;
-  if (allow_wide && cfg_in->max_rows > mt::MAX_R && cfg_in->attn_dim == 0 &&
+  if (allow_wide && (cfg_in->max_rows > mt::MAX_R || !narrow_fits) && cfg_in->attn_dim == 0 &&
       cfg_in->max_rows * cfg_in->top_k <= mt::MAX_P) {
     HIPCHK(nullptr, hipFuncGetAttributes(&fa, (const void*)mt::moe_tail_kernel_gm_w));
     wide = lds_plan_wide(cfg_in, cfg_in->max_rows, G, TC, fa.sharedSizeBytes, di.lds_per_block, &wplan);
   }
+  if (!narrow_fits && !wide)
+    return fail(nullptr, MOE_TAIL_EUNSUPPORTED, "needs %zu B of LDS, device has %zu", plan.dyn + fa.sharedSizeBytes,
+                di.lds_per_block);
   memset(h, 0, sizeof(*h));
   h->cfg = *cfg;
   h->max_rows_call = cfg_in->max_rows;
   h->wide = wide;
+  h->wide_only = !narrow_fits;
   h->wplan = wplan;
   h->wlds_dyn = wide ? wplan.dyn : 0;
   h->device = dev;
@@ -423,7 +428,7 @@ static moe_tail_status prepare_kernels(const moe_tail_t* h, const DevInfo& di) {
     HIPCHK(nullptr, hipFuncSetAttribute(k_all[k], hipFuncAttributeMaxDynamicSharedMemorySize, lim));
   }
   const bool xl = h->plan.xn_lds;
-  for (int k = xl ? 0 : 8; k < (h->wide ? 16 : xl ? 8 : 12); ++k) {
+  for (int k = h->wide_only ? 12 : xl ? 0 : 8; k < (h->wide ? 16 : xl ? 8 : 12); ++k) {
     if (xl && k >= 8 && k < 12) continue;
     const size_t dyn = k >= 12 ? h->wlds_dyn : h->lds_dyn;
     int nb = 0;
@@ -480,7 +485,7 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // One launch: narrow over rows <= MAX_R, or wide over more (handles with wide set).
 static moe_tail_status run_launch(moe_tail_t* h, int32_t rows, const moe_tail_args* a, void* stream) {
   const moe_tail_config& c = h->cfg;
-  const bool wide = rows > c.max_rows && h->wide;
+  const bool wide = h->wide && (rows > c.max_rows || h->wide_only);
   const int lim = wide ? h->max_rows_call : c.max_rows;
   if (rows < 1 || rows > lim) return fail(h, MOE_TAIL_EINVAL, "rows %d outside 1..%d", rows, lim);
   const LdsPlan& pl = wide ? h->wplan : h->plan;
@@ -738,9 +743,11 @@ extern "C" moe_tail_status moe_tail_run_noalloc(const moe_tail_config* cfg, int3
                   L.total, sizeof(scratch));
     // the residency check passed at this dynamic LDS size or a larger one
     size_t& done = h.plan.xn_lds ? d.lds_ready : d.lds_ready_gm;
-    if (h.lds_dyn > done || !done || (h.wide && (h.wlds_dyn > d.lds_ready_w || !d.lds_ready_w))) {
+    const bool need_n = !h.wide_only && (h.lds_dyn > done || !done);
+    const bool need_w = h.wide && (h.wlds_dyn > d.lds_ready_w || !d.lds_ready_w);
+    if (need_n || need_w) {
       if ((st = prepare_kernels(&h, d.info)) != MOE_TAIL_OK) return st;
-      done = h.lds_dyn > done ? h.lds_dyn : done;
+      if (!h.wide_only && h.lds_dyn > done) done = h.lds_dyn;
       if (h.wide && h.wlds_dyn > d.lds_ready_w) d.lds_ready_w = h.wlds_dyn;
     }
     place_scratch(&h, L, d.ptr);

@@ -178,10 +178,12 @@ moe_tail_status moe_tail_create(const moe_tail_config* cfg, moe_tail_t** out);
  * distinct expert streams once per call; where rows are MFMA columns (router
  * and shared gate/up, shared down) a weight load feeds two 16-column tiles,
  * and an expert picked by more than 16 rows runs as one slot per 16 of them
- * (its weights are read once per slot, the second time mostly from L2).
- * Otherwise such calls run as ceil(rows / 16) narrow launches over balanced
- * row ranges, in order on the stream, each streaming its own experts.  A
- * row's outputs are the same bits at every width.  Graph-capturable:
+ * (its weights are read once per slot).  A handle whose 16-row narrow
+ * launch does not fit in LDS (many picks per row) runs every call as a wide
+ * launch.  Otherwise calls above 16 rows run as ceil(rows / 16) narrow
+ * launches over balanced row ranges, in order on the stream, each streaming
+ * its own experts.  A row's outputs are the same bits at every width.
+ * Graph-capturable:
  * the handle's per-call epoch lives in device memory, so replays need no
  * host work.  Calls on one handle must be ordered (one stream at a time).
  * Argument errors are returned synchronously and nothing is enqueued; a

@@ -59,3 +59,21 @@ def gapped_rows(cfg, rw: dict, rho: float = None, max_attempts: int = 64):
 @functools.lru_cache(maxsize=2)
 def weights(name: str):
     return synth.make_weights(synth.CONFIGS[name])
+
+
+def oracle_rows(x, r, w, cfg):
+    """oracle.moe_tail on rows x, r, with the rows split over threads (the
+    oracle's C code releases the interpreter lock).  Rows are independent in
+    the method, so each thread's rows are whole calls and the results are
+    concatenated row by row."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    R = x.shape[0]
+    nt = max(1, min(R, len(os.sched_getaffinity(0)), 16))
+    bounds = [(i * R // nt, (i + 1) * R // nt) for i in range(nt)]
+    with ThreadPoolExecutor(max_workers=nt) as pool:
+        parts = list(pool.map(lambda b: oracle.moe_tail(x[b[0]:b[1]], None if r is None else r[b[0]:b[1]], w,
+                                                        cfg.with_rows(b[1] - b[0])), bounds))
+    return {k: (np.concatenate([p[k] for p in parts]) if isinstance(parts[0][k], np.ndarray) and parts[0][k].ndim >= 1
+                and parts[0][k].shape[0] == bounds[0][1] - bounds[0][0] else parts[0][k]) for k in parts[0]}
+

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from cases import gapped_rows, weights
+from cases import gapped_rows, oracle_rows, weights
 from decode_moe_layer_amd import synth
 from gpu_harness import check_against_oracle, device_weights, handle_for, run
 
@@ -280,7 +280,7 @@ def test_parity_above_16_rows(name, rows, max_rows):
     _say("rows", name, rows, "max_rows", max_rows)
     w = weights(name)
     x, r, _ = gapped_rows(cfg, w)
-    o = oracle.moe_tail(x, r, w, cfg)
+    o = oracle_rows(x, r, w, cfg)
     h = handle_for(cfg, max_rows=max_rows)
     g = run(h, cfg, device_weights(name), x, r)
     assert h.get_error() == 0

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from cases import gapped_rows, weights
+from cases import gapped_rows, oracle_rows, weights
 from decode_moe_layer_amd import synth
 from gpu_harness import check_against_oracle, device_weights, handle_for, run
 
@@ -83,3 +83,35 @@ def test_wide_all_options(name, rows):
     for k in ("ids", "w", "out", "res_out", "y_routed", "y_shared", "logits"):
         np.testing.assert_array_equal(g[k][:16], g16[k], err_msg=k)
     del dw, h
+
+
+# (config, max_rows): c1's shard at 32 rows with top-16 is 512 picks, the most
+# a wide launch takes; at that top-k even 16 rows do not fit a narrow launch's
+# LDS, so the handle runs every call wide, its routed activations staged in
+# groups.  A small shard at 32 rows with top-17 is 544 picks: narrow launches.
+PICK_LIMIT = {
+    "wide_512": (dataclasses.replace(synth.CONFIGS["c1"].with_rows(32), topk=16), 32),
+    "narrow_544": (synth.Config("narrow_544", 12, 32, 512, 64, 17, 64, 64), 32),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PICK_LIMIT))
+def test_wide_pick_limit(case):
+    """Parity with the oracle at the wide launch's pick limit and just past
+    it, and the first 16 rows equal a 16-row call, bit for bit."""
+    cfg, max_rows = PICK_LIMIT[case]
+    _say("pick limit", case, cfg.rows, "rows, top", cfg.topk)
+    w = weights("c1") if case == "wide_512" else synth.make_weights(cfg)
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle_rows(x, r, w, cfg)
+    from gpu_harness import dev
+
+    dw = device_weights("c1") if case == "wide_512" else {k: dev(v) for k, v in w.items()}
+    h = handle_for(cfg, max_rows=max_rows)
+    g = run(h, cfg, dw, x, r)
+    assert h.get_error() == 0
+    check_against_oracle(g, o, cfg)
+    c16 = cfg.with_rows(16)
+    g16 = run(handle_for(c16), c16, dw, x[:16], r[:16])
+    for k in ("ids", "w", "out", "res_out", "y_routed", "y_shared", "logits"):
+        np.testing.assert_array_equal(g[k][:16], g16[k], err_msg=k)
