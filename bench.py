@@ -361,6 +361,7 @@ def main():
     if args.sweep:
         for rows in (1, 2, 4, 16):
             sweep.append(measure("c1", rows))
+        sweep.append(measure("c1", 16, shuf=True))  # 16 rows with the headline's gate/up layout
         sweep.append(head)
         sweep.append(measure("c2", 8))  # the same with row-major gate/up codes
         sweep.append(measure("c3", 4))
@@ -370,6 +371,7 @@ def main():
         sweep.append(measure("c2", 8, 0, 1))
         sweep.append(measure("c1", 1, 0, 1))
         sweep.append(measure("c1", 32))
+        sweep.append(measure("c1", 32, shuf=True))
         sweep.append(measure("c2", 8, front=True))
     copy_gbps = copy_bandwidth(torch)
     cpu = cpu_baseline(cfgs["c2"]) if args.cpu else None

@@ -292,11 +292,12 @@ def test_parity_above_16_rows(name, rows, max_rows):
         np.testing.assert_array_equal(g[k][:r1], g1[k], err_msg=k)
 
 
-@pytest.mark.parametrize("name,rows", [("c0", 2), ("c1", 8), ("c3", 4), ("c4", 16)])
+@pytest.mark.parametrize("name,rows", [("c0", 2), ("c1", 8), ("c3", 4), ("c4", 16), ("c1", 24)])
 def test_unit_blocked_w13_matches_row_major(name, rows):
     """The same MXFP4 gate/up codes in the unit-blocked layout give the same
     GPU outputs, bit for bit, as in the row-major one (every kernel path:
-    routed sums by every reader, xn in LDS, sigmoid keys, xn from global)."""
+    routed sums by every reader, xn in LDS, sigmoid keys, xn from global,
+    a wide launch)."""
     from gpu_harness import dev
 
     cfg = synth.CONFIGS[name].with_rows(rows)
