@@ -1,6 +1,6 @@
 """Determinism under load: one captured graph of calls of mixed widths
-(8, 1, 3, 8, 2, 5 and 16 rows on one handle), replayed until more than
-10,000 calls have run.  Every replay is compared with the eager results of
+(8, 1, 3, 8, 2, 5, 16, 24 and 32 rows on one handle; the last two are wide
+launches), replayed until more than 10,000 calls have run.  Every replay is compared with the eager results of
 the same calls, element for element, and folded into a digest; the check
 stops at the first mismatch and names the replay.  A perturbation control
 (one bit of one input changed between replays) must change the digest, so
@@ -13,28 +13,27 @@ validation section (replays that match the eager hash)."""
 import numpy as np
 import pytest
 
-import oracle
-from cases import gapped_rows, weights
+from cases import gapped_rows, oracle_rows, weights
 from decode_moe_layer_amd import binding, synth
 from gpu_harness import check_against_oracle, dev, device_weights, handle_for, run
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = (8, 1, 3, 8, 2, 5, 16)
-CALLS = 10_010  # 1430 replays of the 7 calls
+WIDTHS = (8, 1, 3, 8, 2, 5, 16, 24, 32)
+CALLS = 10_010  # 1113 replays of the 9 calls
 CHECK_EVERY = 50  # replays between host checks of the running mismatch flag
 
 
 def _setup():
     t = pytest.importorskip("torch")
-    cfg = synth.CONFIGS["c1"].with_rows(16)
+    cfg = synth.CONFIGS["c1"].with_rows(32)
     w = weights("c1")
     x, r, _ = gapped_rows(cfg, w)
-    h = handle_for(cfg, max_rows=16)
+    h = handle_for(cfg, max_rows=32)
     dw = device_weights("c1")
     eager = [run(h, cfg, dw, x[:n], r[:n], rows=n) for n in WIDTHS]
-    # the eager results themselves meet the parity bar (16 rows)
-    check_against_oracle(eager[-1], oracle.moe_tail(x, r, w, cfg), cfg)
+    # the eager results themselves meet the parity bar (all 32 rows)
+    check_against_oracle(eager[-1], oracle_rows(x, r, w, cfg), cfg)
     xd, rd = dev(x), dev(r)
     outs = [t.empty((n, cfg.hidden), dtype=t.int16, device="cuda") for n in WIDTHS]
     refs = [t.from_numpy(e["out"].view(np.int16)).to("cuda") for e in eager]
