@@ -115,3 +115,22 @@ def test_wide_pick_limit(case):
     g16 = run(handle_for(c16), c16, dw, x[:16], r[:16])
     for k in ("ids", "w", "out", "res_out", "y_routed", "y_shared", "logits"):
         np.testing.assert_array_equal(g[k][:16], g16[k], err_msg=k)
+
+
+def test_wide_deadline_drill_then_recovery_on_the_same_handle():
+    """A wide launch (c0's shard, 24 rows) whose workgroup 3 is held at its
+    first cross-workgroup wait on the first call only: the deadline fires,
+    the error reads ETIMEOUT, and the same handle's next call is at parity."""
+    from decode_moe_layer_amd import binding
+
+    cfg = synth.CONFIGS["c0"].with_rows(24)
+    w = weights("c0")
+    x, r, _ = gapped_rows(cfg, w)
+    o = oracle_rows(x, r, w, cfg)
+    dw = device_weights("c0")
+    h = handle_for(cfg, max_rows=32, deadline_us=20000, debug_flags=binding.DEBUG_STALL_ONCE, debug_block=3)
+    run(h, cfg, dw, x, r)
+    assert h.get_error() == binding.ETIMEOUT
+    g = run(h, cfg, dw, x, r)
+    assert h.get_error() == binding.OK
+    check_against_oracle(g, o, cfg)
